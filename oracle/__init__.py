@@ -1,0 +1,21 @@
+"""CPU oracle for the paged decode path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import
+this package. It imports nothing from the HIP library and the library imports nothing from it.
+"""
+from .paged_attention import (  # noqa: F401
+    attention_one_query,
+    blockwise_online_ref,
+    copy_blocks_ref,
+    gather_sequence_kv,
+    k_offset,
+    merge_partition_states_ref,
+    paged_decode_ref,
+    partition_states_ref,
+    reshape_and_cache_ref,
+    slot_of,
+    storage_dtype,
+    to_f64,
+    token_kv,
+    v_offset,
+)

@@ -1,0 +1,302 @@
+"""CPU oracle for the paged KV-cache decode path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this module. It shares no code with the HIP library (no kernels,
+headers, helpers, constants or layout tables) and imports nothing from it; the library never
+imports it.
+
+Everything is plain numpy in float64. Stored fp32 / fp16 / bf16 values are widened exactly to
+float64 before any arithmetic. Nothing is blocked, fused or reordered beyond what the cited
+definitions state.
+
+Sources, cited by page title and section (the same four pages throughout):
+  [wiki]  "PagedAttention" (newikis.com/ko/PagedAttention), section "수학적 공식" (mathematical
+          formulation): the dense causal attention of one query token i (weights a_ij, output
+          o_i summed over t = 1..i) and its blocked form (K_j, V_j of B tokens each; A_ij,
+          o_i summed over the first ceil(i/B) blocks).
+  [anal]  "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net), §2 (KV blocks of
+          B tokens in scattered physical memory, on-demand allocation), §3 (the block-wise
+          kernel gives the same result as ordinary attention, only partial sums are blocked),
+          the block-table lookup pseudocode (running max starting at -inf, running denominator,
+          running output, final division), §4 (copy-on-write of a shared block).
+  [blog]  "PagedAttention 논문 쉽게 읽기" (iplexlaw.co.kr), §2: a token is written into the free
+          slot of its sequence's last block; ②: copy-on-write of a shared last block.
+  [dev]   "추론 엔진에서의 메모리 가상화: PagedAttention과 메모리 단편화의 제거" (molayo1419.me):
+          two preallocated pools key_cache / value_cache; copy-on-write allocates a fresh block,
+          copies the old contents, remaps the writer's table entry.
+
+Readings where the pages leave a step open (each is listed with its reason in the design notes):
+  * The query of the decode step is the sequence's newest token, so it attends to all
+    ``ctx`` cached tokens, itself included (the dense formula sums t = 1..i).
+  * The blocked formula's last block K_j runs past token i; those slots are excluded (weight 0),
+    as the dense formula, which stops at t = i, requires.
+  * The blocked denominator sums exp over every score of blocks 1..ceil(i/B) (all entries), which
+    is the dense denominator.
+  * The scale is the caller's float32 ``scale`` (1/sqrt(d) in every workload), widened exactly.
+  * Grouped-query attention (not on the pages): query head h reads KV head h // (Hq / Hkv).
+  * ctx = 0 gives a zero output.
+
+The physical pool layout is the library's choice, fixed by its header; ``k_offset`` and
+``v_offset`` below restate it from that description and are pinned by layout properties in
+the tests (a bijection, contiguous 4 KiB tiles, 1 KiB key chunk rows), and against the library
+only through parity.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------------------------
+# Stored dtypes
+# ---------------------------------------------------------------------------------------------
+
+_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+_ESZ = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def storage_dtype(dtype: str):
+    """numpy array dtype holding stored elements (bf16 is held as its 16 raw bits)."""
+    return _STORAGE[dtype]
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of stored fp32 / fp16 / bf16 elements to float64.
+
+    bf16 is the upper half of an IEEE binary32, so its 16 bits shifted left by 16 are the
+    binary32 of the same value.
+    """
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float32, copy=False).astype(np.float64)
+    if dtype == "f16":
+        return a.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        bits = a.view(np.uint16).astype(np.uint32) << np.uint32(16)
+        with np.errstate(invalid="ignore"):     # signalling-NaN bit patterns stay NaN
+            return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------------------------
+# Physical pool layout (the library's documented index functions, restated independently)
+# ---------------------------------------------------------------------------------------------
+
+def k_offset(b, h, t, i, *, num_kv_heads: int, block_size: int, head_dim: int, esz: int):
+    """Element offset of key (physical block b, KV head h, slot t, dim i) in the key pool.
+
+    The (b, h) tile of block_size*head_dim elements starts at (b*Hkv + h)*B*d. Inside it the
+    head dimension is cut into 64-byte chunks of W = 64/esz elements; chunk c holds, for slot
+    0..B-1 in turn, that slot's W elements, so element (t, i) sits at (i//W)*B*W + t*W + i%W.
+    """
+    W = 64 // esz
+    tile = block_size * head_dim
+    return ((np.asarray(b, dtype=np.int64) * num_kv_heads + h) * tile
+            + (np.asarray(i) // W) * (block_size * W) + np.asarray(t) * W + np.asarray(i) % W)
+
+
+def v_offset(b, h, t, i, *, num_kv_heads: int, block_size: int, head_dim: int):
+    """Element offset of value (b, h, t, i) in the value pool: tile (b*Hkv + h), row t, column i."""
+    return ((np.asarray(b, dtype=np.int64) * num_kv_heads + h) * block_size
+            + np.asarray(t)) * head_dim + np.asarray(i)
+
+
+def _flat(pool: np.ndarray) -> np.ndarray:
+    return pool.reshape(-1)
+
+
+def token_kv(k_pool, v_pool, blocks, slots, *, dtype, num_kv_heads, block_size, head_dim):
+    """Keys and values of the given (physical block, slot) pairs: two float64 [n, Hkv, d]."""
+    esz = _ESZ[dtype]
+    b = np.asarray(blocks, dtype=np.int64)[:, None, None]
+    t = np.asarray(slots, dtype=np.int64)[:, None, None]
+    h = np.arange(num_kv_heads)[None, :, None]
+    i = np.arange(head_dim)[None, None, :]
+    ko = k_offset(b, h, t, i, num_kv_heads=num_kv_heads, block_size=block_size,
+                  head_dim=head_dim, esz=esz)
+    vo = v_offset(b, h, t, i, num_kv_heads=num_kv_heads, block_size=block_size,
+                  head_dim=head_dim)
+    return to_f64(_flat(k_pool)[ko], dtype), to_f64(_flat(v_pool)[vo], dtype)
+
+
+def gather_sequence_kv(k_pool, v_pool, block_table_row, ctx, *, dtype, num_kv_heads,
+                       block_size, head_dim):
+    """Logical keys/values of one sequence's first ``ctx`` tokens through its block table.
+
+    Token t (0-based) lives in logical block t // B, which the table maps to a physical block,
+    at slot t % B ([anal] §2 and the lookup pseudocode; [wiki] blocked K_j, V_j).
+    Returns two float64 arrays [ctx, Hkv, d].
+    """
+    t = np.arange(int(ctx))
+    phys = np.asarray(block_table_row)[t // block_size]
+    return token_kv(k_pool, v_pool, phys, t % block_size, dtype=dtype,
+                    num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
+
+
+# ---------------------------------------------------------------------------------------------
+# Attention: the plain definition
+# ---------------------------------------------------------------------------------------------
+
+def attention_one_query(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * K q) weighted sum of the rows of V, in float64 ([wiki] dense form).
+
+    q [d], K [n, d], V [n, d]. Subtracting the maximum score before exp leaves the weights
+    unchanged and keeps exp finite. n = 0 gives zeros.
+    """
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1])
+    z = scale * (K @ q)
+    w = np.exp(z - z.max())
+    return (w @ V) / w.sum()
+
+
+def paged_decode_ref(query, k_pool, v_pool, block_tables, context_lens, scale, *, dtype,
+                     num_kv_heads, block_size, head_dim, seqs=None, heads=None):
+    """Decode attention of every (sequence, query head) over its paged KV cache.
+
+    query: stored [S, Hq, d]; pools: stored, any shape with NB*Hkv*B*d elements in the library
+    layout; block_tables int [S, maxb]; context_lens int [S]; scale: the caller's float32.
+    ``seqs`` / ``heads`` select a subset (for sampled checks at full size).
+    Returns float64 [len(seqs), len(heads), d].
+    """
+    q64 = to_f64(query, dtype)
+    S, Hq, d = q64.shape
+    G = Hq // num_kv_heads
+    scale64 = float(np.float32(scale))
+    seqs = range(S) if seqs is None else list(seqs)
+    heads = range(Hq) if heads is None else list(heads)
+    out = np.zeros((len(seqs), len(heads), d))
+    for n, s in enumerate(seqs):
+        ctx = int(context_lens[s])
+        K, V = gather_sequence_kv(k_pool, v_pool, block_tables[s], ctx, dtype=dtype,
+                                  num_kv_heads=num_kv_heads, block_size=block_size,
+                                  head_dim=head_dim)
+        for m, h in enumerate(heads):
+            g = h // G
+            out[n, m] = attention_one_query(q64[s, h], K[:, g, :], V[:, g, :], scale64)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# The pages' block-by-block loop (a second form, used to check the first)
+# ---------------------------------------------------------------------------------------------
+
+def blockwise_online_ref(q, k_pool, v_pool, block_table_row, ctx, scale, g, *, dtype,
+                         num_kv_heads, block_size, head_dim):
+    """One query head over one sequence, block by block with a running softmax.
+
+    Follows the block-table lookup pseudocode of [anal]: output, denominator and running
+    maximum start at 0, 0 and -inf; for each logical block, look up its physical block, take its
+    keys and values, score them, fold them into the running state; divide at the end. The
+    running-state update, which the pseudocode names but does not spell out, is the usual one:
+    new max m' = max(m, block scores); old state rescaled by exp(m - m'); new terms weighted
+    by exp(score - m'). Slots at or past ``ctx`` in the last block are left out.
+    q: float64 [d]. Returns float64 [d].
+    """
+    scale64 = float(np.float32(scale))
+    out = np.zeros(head_dim)
+    denom = 0.0
+    running_max = -np.inf
+    num_blocks = -(-int(ctx) // block_size)
+    for j in range(num_blocks):
+        phys = int(block_table_row[j])
+        valid = min(block_size, int(ctx) - j * block_size)
+        slots = np.arange(valid)
+        K, V = token_kv(k_pool, v_pool, np.full(valid, phys), slots, dtype=dtype,
+                        num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
+        s = scale64 * (K[:, g, :] @ q)
+        new_max = max(running_max, float(s.max()))
+        rescale = np.exp(running_max - new_max)     # exp(-inf) = 0 on the first block
+        p = np.exp(s - new_max)
+        denom = denom * rescale + p.sum()
+        out = out * rescale + p @ V[:, g, :]
+        running_max = new_max
+    if num_blocks == 0:
+        return out
+    return out / denom
+
+
+# ---------------------------------------------------------------------------------------------
+# Split over context partitions and the merge of their states
+# ---------------------------------------------------------------------------------------------
+
+def partition_states_ref(q, K, V, scale, partition_tokens):
+    """Softmax state (m, l, acc) of each run of ``partition_tokens`` consecutive tokens.
+
+    m = max score in the run, l = sum of exp(score - m), acc = sum of exp(score - m) * v.
+    q [d], K/V [n, d] float64.
+    """
+    scale64 = float(np.float32(scale))
+    states = []
+    for start in range(0, K.shape[0], partition_tokens):
+        z = scale64 * (K[start:start + partition_tokens] @ q)
+        m = float(z.max())
+        w = np.exp(z - m)
+        states.append((m, float(w.sum()), w @ V[start:start + partition_tokens]))
+    return states
+
+
+def merge_partition_states_ref(states):
+    """Combine partition states: with M the largest m, o = sum e^(m_p-M) acc_p / sum e^(m_p-M) l_p.
+
+    Exact because every partial sum only needs rescaling to a common maximum ([anal] §3: the
+    blocked computation differs from ordinary attention only in how partial sums are grouped).
+    """
+    M = max(m for m, _, _ in states)
+    num = sum(np.exp(m - M) * acc for m, _, acc in states)
+    den = sum(np.exp(m - M) * l for m, l, _ in states)
+    return num / den
+
+
+# ---------------------------------------------------------------------------------------------
+# Cache writes and block copies
+# ---------------------------------------------------------------------------------------------
+
+def slot_of(block_table_row, pos: int, block_size: int) -> int:
+    """Physical slot of token position ``pos``: the table's block for pos // B, offset pos % B."""
+    return int(block_table_row[pos // block_size]) * block_size + pos % block_size
+
+
+def reshape_and_cache_ref(k_pool, v_pool, key, value, block_tables, token_seq, token_pos, *,
+                          dtype, num_kv_heads, block_size, head_dim):
+    """Copies of the pools with each new token's key/value written into its slot.
+
+    Token n belongs to sequence token_seq[n] at position token_pos[n] (negative = skip). Its
+    slot is the one ``slot_of`` names ([blog] §2: the token goes into its block's free slot).
+    Elements are copied bit for bit. key/value: stored [T, Hkv, d].
+    """
+    esz = _ESZ[dtype]
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    kf, vf = _flat(k_out), _flat(v_out)
+    key = np.asarray(key)
+    value = np.asarray(value)
+    i = np.arange(head_dim)
+    for n in range(len(token_seq)):
+        pos = int(token_pos[n])
+        if pos < 0:
+            continue
+        slot = slot_of(block_tables[int(token_seq[n])], pos, block_size)
+        b, t = slot // block_size, slot % block_size
+        for h in range(num_kv_heads):
+            kf[k_offset(b, h, t, i, num_kv_heads=num_kv_heads, block_size=block_size,
+                        head_dim=head_dim, esz=esz)] = key[n, h]
+            vf[v_offset(b, h, t, i, num_kv_heads=num_kv_heads, block_size=block_size,
+                        head_dim=head_dim)] = value[n, h]
+    return k_out, v_out
+
+
+def copy_blocks_ref(k_pool, v_pool, pairs, *, dtype, num_kv_heads, block_size, head_dim):
+    """Copies of the pools where, for each (src, dst) pair, block dst receives all of block
+    src's key and value elements (every KV head, every slot), bit for bit ([dev] and [anal] §4:
+    the copy-on-write duplicate of a shared block)."""
+    esz = _ESZ[dtype]
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    kf, vf = _flat(k_out), _flat(v_out)
+    h = np.arange(num_kv_heads)[:, None, None]
+    t = np.arange(block_size)[None, :, None]
+    i = np.arange(head_dim)[None, None, :]
+    kw = dict(num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        kf[k_offset(dst, h, t, i, esz=esz, **kw)] = kf[k_offset(src, h, t, i, esz=esz, **kw)]
+        vf[v_offset(dst, h, t, i, **kw)] = vf[v_offset(src, h, t, i, **kw)]
+    return k_out, v_out

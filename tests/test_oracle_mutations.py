@@ -1,0 +1,192 @@
+"""Plant plausible mistakes in the oracle (on the CPU, through monkeypatch) and check that at
+least one pin fails for each: the pins are strong enough to catch a dropped term, a wrong sign
+or index, or a swapped operand."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.paged_attention as pa_mod
+from oracle_pins import ALL_PINS
+
+_orig = {name: getattr(pa_mod, name) for name in dir(pa_mod) if not name.startswith("__")}
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(pa_mod, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def m_exp_sign(mp):
+    def f(q, K, V, scale):
+        if K.shape[0] == 0:
+            return np.zeros(V.shape[1])
+        z = scale * (K @ q)
+        w = np.exp(-(z - z.max()))
+        return (w @ V) / w.sum()
+    _patch(mp, "attention_one_query", f)
+
+
+def m_denominator(mp):
+    def f(q, K, V, scale):
+        if K.shape[0] == 0:
+            return np.zeros(V.shape[1])
+        z = scale * (K @ q)
+        w = np.exp(z - z.max())
+        return (w @ V) / (w.sum() + 1.0)
+    _patch(mp, "attention_one_query", f)
+
+
+def m_keys_as_values(mp):
+    def f(q, K, V, scale):
+        if K.shape[0] == 0:
+            return np.zeros(V.shape[1])
+        z = scale * (K @ q)
+        w = np.exp(z - z.max())
+        return (w @ K) / w.sum()
+    _patch(mp, "attention_one_query", f)
+
+
+def m_no_scale(mp):
+    orig = _orig["attention_one_query"]
+    _patch(mp, "attention_one_query", lambda q, K, V, scale: orig(q, K, V, 1.0))
+
+
+def m_scale_twice(mp):
+    orig = _orig["attention_one_query"]
+    _patch(mp, "attention_one_query", lambda q, K, V, scale: orig(q, K, V, scale * scale))
+
+
+def m_head_modulo(mp):
+    def f(query, k_pool, v_pool, block_tables, context_lens, scale, *, dtype, num_kv_heads,
+          block_size, head_dim, seqs=None, heads=None):
+        q64 = pa_mod.to_f64(query, dtype)
+        S, Hq, d = q64.shape
+        scale64 = float(np.float32(scale))
+        seqs = range(S) if seqs is None else list(seqs)
+        heads = range(Hq) if heads is None else list(heads)
+        out = np.zeros((len(seqs), len(heads), d))
+        for n, s in enumerate(seqs):
+            K, V = pa_mod.gather_sequence_kv(k_pool, v_pool, block_tables[s], int(context_lens[s]),
+                                             dtype=dtype, num_kv_heads=num_kv_heads,
+                                             block_size=block_size, head_dim=head_dim)
+            for m, h in enumerate(heads):
+                g = h % num_kv_heads
+                out[n, m] = pa_mod.attention_one_query(q64[s, h], K[:, g], V[:, g], scale64)
+        return out
+    _patch(mp, "paged_decode_ref", f)
+
+
+def _gather_with(block_of, slot_of):
+    def f(k_pool, v_pool, row, ctx, *, dtype, num_kv_heads, block_size, head_dim):
+        t = np.arange(int(ctx))
+        phys = np.asarray(row)[block_of(t, block_size)]
+        return pa_mod.token_kv(k_pool, v_pool, phys, slot_of(t, block_size), dtype=dtype,
+                               num_kv_heads=num_kv_heads, block_size=block_size,
+                               head_dim=head_dim)
+    return f
+
+
+def m_gather_block_index(mp):
+    _patch(mp, "gather_sequence_kv", _gather_with(lambda t, B: t % B, lambda t, B: t % B))
+
+
+def m_gather_slot_index(mp):
+    _patch(mp, "gather_sequence_kv", _gather_with(lambda t, B: t // B, lambda t, B: (t + 1) % B))
+
+
+def m_gather_one_past(mp):
+    orig = _orig["gather_sequence_kv"]
+
+    def f(k_pool, v_pool, row, ctx, **kw):
+        n = int(ctx)
+        return orig(k_pool, v_pool, row, n + 1 if n % kw["block_size"] else n, **kw)
+    _patch(mp, "gather_sequence_kv", f)
+
+
+def m_k_offset_swapped(mp):
+    def f(b, h, t, i, *, num_kv_heads, block_size, head_dim, esz):
+        W = 64 // esz
+        tile = block_size * head_dim
+        return ((np.asarray(b, dtype=np.int64) * num_kv_heads + h) * tile
+                + (np.asarray(i) // W) * (block_size * W) + np.asarray(i) % W * block_size
+                + np.asarray(t))
+    _patch(mp, "k_offset", f)
+
+
+def m_v_offset_transposed(mp):
+    def f(b, h, t, i, *, num_kv_heads, block_size, head_dim):
+        return ((np.asarray(b, dtype=np.int64) * num_kv_heads + h) * block_size * head_dim
+                + np.asarray(i) * block_size + np.asarray(t))
+    _patch(mp, "v_offset", f)
+
+
+def m_slot_swapped(mp):
+    _patch(mp, "slot_of", lambda row, pos, B: int(row[pos % B]) * B + pos // B)
+
+
+def m_copy_only_keys(mp):
+    def f(k_pool, v_pool, pairs, *, dtype, num_kv_heads, block_size, head_dim):
+        k2, _ = _orig["copy_blocks_ref"](k_pool, v_pool, pairs, dtype=dtype,
+                                         num_kv_heads=num_kv_heads, block_size=block_size,
+                                         head_dim=head_dim)
+        return k2, np.array(v_pool, copy=True)
+    _patch(mp, "copy_blocks_ref", f)
+
+
+def m_merge_no_rescale_l(mp):
+    def f(states):
+        M = max(m for m, _, _ in states)
+        num = sum(np.exp(m - M) * acc for m, _, acc in states)
+        den = sum(l for _, l, _ in states)
+        return num / den
+    _patch(mp, "merge_partition_states_ref", f)
+
+
+def m_online_no_rescale(mp):
+    def f(q, k_pool, v_pool, row, ctx, scale, g, *, dtype, num_kv_heads, block_size, head_dim):
+        scale64 = float(np.float32(scale))
+        out = np.zeros(head_dim); denom = 0.0; mx = -np.inf
+        for j in range(-(-int(ctx) // block_size)):
+            valid = min(block_size, int(ctx) - j * block_size)
+            K, V = pa_mod.token_kv(k_pool, v_pool, np.full(valid, int(row[j])), np.arange(valid),
+                                   dtype=dtype, num_kv_heads=num_kv_heads,
+                                   block_size=block_size, head_dim=head_dim)
+            s = scale64 * (K[:, g] @ q)
+            new = max(mx, float(s.max()))
+            c = np.exp(mx - new)
+            p = np.exp(s - new)
+            denom = denom * c + p.sum()
+            out = out + p @ V[:, g]
+            mx = new
+        return out / denom
+    _patch(mp, "blockwise_online_ref", f)
+
+
+def m_bf16_shift(mp):
+    orig = _orig["to_f64"]
+
+    def f(a, dtype):
+        if dtype == "bf16":
+            bits = np.asarray(a).view(np.uint16).astype(np.uint32) << np.uint32(15)
+            return bits.view(np.float32).astype(np.float64)
+        return orig(a, dtype)
+    _patch(mp, "to_f64", f)
+
+
+MUTATIONS = [m_exp_sign, m_denominator, m_keys_as_values, m_no_scale, m_scale_twice,
+             m_head_modulo, m_gather_block_index, m_gather_slot_index, m_gather_one_past,
+             m_k_offset_swapped, m_v_offset_transposed, m_slot_swapped, m_copy_only_keys,
+             m_merge_no_rescale_l, m_online_no_rescale, m_bf16_shift]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__ for m in MUTATIONS])
+def test_planted_mistake_is_caught(mutation, monkeypatch):
+    mutation(monkeypatch)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(oracle)
+        except Exception as e:  # an assertion, or a crash the mistake causes
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught {mutation.__name__}"

@@ -1,0 +1,172 @@
+"""Host logic: the block manager (free list, reference counts, copy-on-write), the synthetic
+workload shapes, and closed-form byte accounting. CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_384_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_cow_worked_example():
+    g = _golden("cow_worked_example.json")
+    B = g["block_size"]
+    fresh = g["fresh_block"]
+    order = np.array(g["prompt_blocks"] + [fresh] + [b for b in range(64)
+                     if b not in g["prompt_blocks"] + [fresh]])
+    bm = wl.BlockManager(64, B, order=order)
+    root = bm.new_sequence()
+    bm.append_tokens(root, g["prompt_tokens"])
+    assert bm.tables[root] == g["prompt_blocks"]
+    a = bm.fork(root)
+    b = bm.fork(root)
+    bm.free_sequence(root)
+    assert all(bm.ref[x] == 2 for x in g["prompt_blocks"])
+    bm.append_tokens(a, 1)
+    exp = g["after_first_write"]
+    assert bm.tables[a] == exp["writer_table"]
+    assert bm.tables[b] == exp["other_table"]
+    assert {str(k): int(bm.ref[k]) for k in (10, 11, 45)} == exp["ref"]
+    assert [list(p) for p in bm.copies] == exp["copies"]
+    # the last sharer writes in place: no further copy
+    bm.append_tokens(b, 1)
+    assert bm.tables[b] == exp["other_table"] and len(bm.copies) == 1
+
+
+def test_opt13b_kv_bytes():
+    g = _golden("kv_sizes.json")["opt13b"]
+    per_tok = wl.kv_bytes_per_token(g["num_layers"], g["hidden"], g["bytes_per_elem"])
+    assert per_tok == g["kv_bytes_per_token"]
+    assert abs(per_tok / 1000 - g["per_token_kb_page"]) / g["per_token_kb_page"] < g["per_token_tolerance"]
+    lo, hi = g["per_sequence_gb_page"]
+    assert lo <= per_tok * g["max_context"] / 1e9 <= hi
+
+
+def test_waste_bounds_and_mean():
+    g = _golden("kv_sizes.json")["waste"]
+    B = g["block_size"]
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, 5000, size=4000)
+    bm = wl.BlockManager(int(sum(-(-int(n) // B) for n in lens)) + 1, B, rng=rng)
+    waste = []
+    for n in lens:
+        s = bm.new_sequence()
+        bm.append_tokens(s, int(n))
+        assert len(bm.tables[s]) == -(-int(n) // B)
+        waste.append(bm.wasted_slots(s))
+    waste = np.array(waste)
+    assert waste.max() <= g["max_wasted_slots"] and waste.min() >= 0
+    # standard error of the mean of a uniform{0..15} is ~4.6/sqrt(4000) = 0.07
+    assert abs(waste.mean() - g["mean_wasted_slots_exact"]) < 0.3
+
+
+def test_waste_fraction_opt13b_shape():
+    bound = _golden("kv_sizes.json")["waste_fraction_bound"]["bound"]
+    b = wl.build_batch(wl.CONFIGS["opt13b_fp16"])
+    allocated = int((b.context_lens.astype(np.int64) + b.wasted_slots).sum())
+    assert b.wasted_slots.sum() / allocated < bound
+
+
+def test_pool_exhaustion_raises():
+    bm = wl.BlockManager(3, 16)
+    s = bm.new_sequence()
+    bm.append_tokens(s, 48)
+    with pytest.raises(wl.PoolExhausted):
+        bm.append_tokens(s, 1)
+
+
+def test_free_returns_blocks():
+    bm = wl.BlockManager(8, 16, rng=np.random.default_rng(1))
+    s = bm.new_sequence()
+    bm.append_tokens(s, 40)
+    assert bm.num_free == 5
+    t = bm.fork(s)
+    bm.free_sequence(s)
+    assert bm.num_free == 5
+    bm.free_sequence(t)
+    assert bm.num_free == 8 and bm.ref.sum() == 0
+
+
+@pytest.mark.parametrize("name,exp", [
+    ("tiny_fp32", dict(dtype="f32", S=4, Hq=4, Hkv=4, d=64, B=16, lo=1, hi=200, NB=64)),
+    ("opt13b_fp16", dict(dtype="f16", S=64, Hq=40, Hkv=40, d=128, B=16, lo=128, hi=2048, NB=8192)),
+    ("gqa_bf16", dict(dtype="bf16", S=256, Hq=32, Hkv=8, d=128, B=16, lo=16, hi=4096, NB=None)),
+    ("cow_fp16", dict(dtype="f16", S=256, Hq=40, Hkv=40, d=128, B=16, lo=521, hi=776, NB=None)),
+    ("long_bf16", dict(dtype="bf16", S=8, Hq=32, Hkv=8, d=128, B=16, lo=16384, hi=32768, NB=None)),
+])
+def test_config_shapes(name, exp):
+    cfg = wl.CONFIGS[name]
+    assert (cfg.dtype, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+            cfg.block_size) == (exp["dtype"], exp["S"], exp["Hq"], exp["Hkv"], exp["d"], exp["B"])
+    b = wl.build_batch(cfg)
+    assert b.context_lens.min() >= exp["lo"] and b.context_lens.max() <= exp["hi"]
+    if exp["NB"] is not None:
+        assert b.num_blocks == exp["NB"]
+    B = cfg.block_size
+    nb = -(-b.context_lens.astype(np.int64) // B)
+    for s in range(cfg.num_seqs):
+        row = b.block_tables[s]
+        assert np.all(row[nb[s]:] == b.poison_block)
+        assert np.all(row[:nb[s]] != b.poison_block)
+        assert np.all((row >= 0) & (row < b.num_blocks))
+    # reference counts equal the number of table entries pointing at each block
+    used = np.concatenate([b.block_tables[s, :nb[s]] for s in range(cfg.num_seqs)])
+    assert np.array_equal(np.bincount(used, minlength=b.num_blocks), b.ref_counts)
+    assert np.array_equal(b.token_pos, b.context_lens - 1)
+    # deterministic
+    b2 = wl.build_batch(cfg)
+    assert np.array_equal(b.block_tables, b2.block_tables)
+    assert np.array_equal(b.context_lens, b2.context_lens)
+
+
+def test_unshared_configs_own_their_blocks():
+    for name in ("tiny_fp32", "opt13b_fp16", "gqa_bf16", "long_bf16"):
+        b = wl.build_batch(wl.CONFIGS[name])
+        assert b.ref_counts.max() == 1 and b.copy_pairs.shape[0] == 0
+
+
+def test_shared_prefix_structure():
+    cfg = wl.CONFIGS["cow_fp16"]
+    b = wl.build_batch(cfg)
+    prompt, lo, hi, n = cfg.ctx[1:]
+    B = cfg.block_size
+    full = prompt // B                       # 32 full prompt blocks, shared by all 8 samples
+    assert prompt % B == 8
+    assert b.copy_pairs.shape == ((cfg.num_seqs // n) * (n - 1), 2)   # 224 pairs
+    for p in range(cfg.num_seqs // n):
+        rows = b.block_tables[p * n:(p + 1) * n]
+        assert np.all(rows[:, :full] == rows[0, :full])
+        assert np.all(b.ref_counts[rows[0, :full]] == n)
+        partial = rows[:, full]
+        assert len(set(partial.tolist())) == n                     # 7 copies + the original
+        srcs = b.copy_pairs[p * (n - 1):(p + 1) * (n - 1), 0]
+        dsts = b.copy_pairs[p * (n - 1):(p + 1) * (n - 1), 1]
+        assert np.all(srcs == partial[n - 1])                     # last sharer kept it
+        assert set(dsts.tolist()) == set(partial[:n - 1].tolist())
+    # copy destinations are unique and never a source
+    d = b.copy_pairs[:, 1]
+    assert len(set(d.tolist())) == d.size and not set(d.tolist()) & set(b.copy_pairs[:, 0].tolist())
+
+
+def test_lognormal_draws():
+    cfg = wl.CONFIGS["gqa_bf16"]
+    b = wl.build_batch(cfg)
+    med = np.median(b.context_lens)
+    assert 800 < med < 1300
+    assert b.context_lens.min() >= 16 and b.context_lens.max() <= 4096
+
+
+def test_kv_bytes_accounting():
+    b = wl.build_batch(wl.CONFIGS["opt13b_fp16"])
+    assert b.kv_bytes() == int(b.context_lens.sum()) * 40 * 128 * 2 * 2
+    # expected value: 64 seqs * mean ctx 1088 * 40 heads * 128 * 2 (K and V) * 2 bytes = 1.43 GB
+    assert abs(b.kv_bytes() / 1.426e9 - 1) < 0.1
