@@ -1,0 +1,242 @@
+"""Benchmark of the paged decode path on one MI355X.
+
+A step is one pass of the whole path over one synthetic decode batch: copy-on-write block
+copies (none in the OPT-13B-shape batch), the cache write of one new token per sequence, the
+per-partition attention kernel and the partition merge. Inputs are resident in HBM before the
+timed region; three independently drawn input sets rotate so that repeated steps are not
+served from the 256 MB Infinity Cache.
+
+Prints one JSON line. ``value`` is KV bytes read per step / step time (GB/s, whole step);
+``roofline`` reports the attention kernel alone (HIP events on its stream) against the 8 TB/s
+HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--partition P]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["paged_kv_cache_384_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_384_amd/csrc/pa_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pa_decode_attention_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def host_storage(t):
+    """Host numpy copy of a tensor's stored elements (bf16 as raw uint16 bits)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_baseline(batch, host, budget_s: float):
+    """The CPU oracle, single-threaded, on as many whole sequences as fit in ``budget_s``."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cfg = batch.cfg
+    kw = dict(dtype=cfg.dtype, num_kv_heads=cfg.num_kv_heads, block_size=cfg.block_size,
+              head_dim=cfg.head_dim)
+    done, kv = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s in range(cfg.num_seqs):
+            oracle.paged_decode_ref(host["query"], host["k_pool"], host["v_pool"],
+                                    batch.block_tables, batch.context_lens, cfg.scale,
+                                    seqs=[s], **kw)
+            done += 1
+            kv += int(batch.context_lens[s]) * cfg.num_kv_heads * cfg.head_dim * 2 * cfg.esz
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {cfg.num_seqs} sequences (all {cfg.num_q_heads} query heads), "
+                      f"{kv / 1e6:.1f} MB of KV in {dt:.1f} s, numpy float64, 1 thread",
+            "seconds": round(dt, 2), "tokens_per_s": round(done / dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="opt13b_fp16")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition size in tokens; -1 = the workload's own setting")
+    ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_384_amd as pa
+    from paged_kv_cache_384_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[args.config]
+    part = cfg.partition_size if args.partition < 0 else args.partition
+    batch = wl.build_batch(cfg)
+    print(f"[bench] {cfg.name}: {cfg.description}", file=sys.stderr, flush=True)
+
+    sets = []
+    for k in range(args.sets):
+        v = wl.make_values(batch, device=dev, seed=k, poison_nan=False)
+        sets.append(v)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    ctx = torch.from_numpy(batch.context_lens).to(dev)
+    tseq = torch.from_numpy(batch.token_seq).to(dev)
+    tpos = torch.from_numpy(batch.token_pos).to(dev)
+    pairs = torch.from_numpy(batch.copy_pairs.reshape(-1)).to(dev)
+    outs = [torch.empty_like(v["query"]) for v in sets]
+    ws_bytes = pa.pa_decode_workspace_bytes(sets[0]["k_pool"], cfg.num_seqs, cfg.num_q_heads,
+                                            cfg.head_dim, batch.max_context_len, part)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kv_bytes = batch.kv_bytes()
+    n_pairs = batch.copy_pairs.shape[0]
+
+    def step(k, ev=None):
+        v = sets[k % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        if n_pairs:
+            pa.pa_copy_blocks(v["k_pool"], v["v_pool"], pairs, head_dim=cfg.head_dim)
+        pa.pa_reshape_and_cache(v["k_pool"], v["v_pool"], v["key"], v["value"], bt, tseq, tpos)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.pa_decode_attention(outs[k % len(sets)], v["query"], v["k_pool"], v["v_pool"], bt, ctx,
+                               cfg.scale, batch.max_context_len, part, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        pa.pa_decode_reduce(outs[k % len(sets)], v["query"], v["k_pool"], v["v_pool"], bt, ctx,
+                            cfg.scale, batch.max_context_len, part, ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps between two events, synchronised on both sides
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(k, evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    cache_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    attn_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    red_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+    attn_avg = float(np.mean(attn_us))
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us);"
+          f" attention {attn_avg:.1f} us (p10 {np.percentile(attn_us, 10):.1f}, p90 "
+          f"{np.percentile(attn_us, 90):.1f}), reduce {np.mean(red_us):.1f} us, cache write "
+          f"{np.mean(cache_us):.1f} us", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {n} byte device copies", file=sys.stderr)
+
+    achieved = kv_bytes / (attn_avg * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": recorded_traffic(cfg.name),
+                "kernel": "decode_attention_kernel", "avg_us": round(attn_avg, 2),
+                "bytes_per_launch": kv_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        host = {name: host_storage(sets[0][name]) for name in ("query", "k_pool", "v_pool")}
+        cpu = cpu_baseline(batch, host, args.cpu_budget)
+
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": "pa_decode KV-read HBM GB/s (fraction of MI355X peak) + decode tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": cfg.num_seqs,
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "block_size": cfg.block_size,
+                   "context_lens": list(cfg.ctx), "num_blocks": batch.num_blocks,
+                   "partition_size": part, "max_context_len": batch.max_context_len,
+                   "kv_bytes_per_step": kv_bytes, "accumulate": "f32",
+                   "copy_pairs": int(n_pairs)},
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
+        "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),
+                      "attention": round(attn_avg, 2),
+                      "partition_reduce": round(float(np.mean(red_us)), 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

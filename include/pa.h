@@ -1,0 +1,197 @@
+/*
+ * pa.h — paged KV-cache decode attention for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Plain C ABI: raw pointers and sizes, no HIP or PyTorch types. Streams are hipStream_t
+ * handles passed as void* (NULL = the default stream). All device buffers are owned by the
+ * caller; the library allocates nothing and keeps no per-call state. Every call is
+ * asynchronous on its stream.
+ *
+ * Sources, cited by page title and section:
+ *   [wiki] "PagedAttention" (newikis.com/ko/PagedAttention), "수학적 공식" (mathematical
+ *          formulation): dense causal attention of query token i, and the same computation
+ *          over key/value blocks K_j, V_j of B tokens, summed over the first ceil(i/B) blocks.
+ *   [anal] "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net): §2 fixed-size
+ *          KV blocks in scattered physical memory addressed through a block table; §3 the
+ *          block-wise attention kernel and its block-table lookup pseudocode; §4 copy-on-write.
+ *   [blog] "PagedAttention 논문 쉽게 읽기" (iplexlaw.co.kr): §2 a new token is written into the
+ *          free slot of its sequence's last block; ② copy-on-write of a shared block.
+ *   [dev]  "추론 엔진에서의 메모리 가상화: PagedAttention과 메모리 단편화의 제거" (molayo1419.me):
+ *          two large preallocated pools, key_cache and value_cache; block_tables handed to the
+ *          attention kernel as a 2-D integer array; the copy in copy-on-write.
+ *
+ * ---------------------------------------------------------------------------------------------
+ * Physical pool layout (chosen for gfx950; the pages' own permuted key layout targets 32-thread
+ * warps and is not used)
+ * ---------------------------------------------------------------------------------------------
+ * Each pool holds num_blocks * num_kv_heads tiles of T = block_size * head_dim elements. Tile
+ * (physical block b, KV head h) is contiguous and starts at element (b * num_kv_heads + h) * T,
+ * so one physical block is num_kv_heads consecutive tiles. Inside a tile, for slot t in
+ * [0, block_size) and head-dimension index i in [0, head_dim):
+ *
+ *   value pool:  element (t, i) at   t * head_dim + i                      (token rows)
+ *   key pool:    with W = 64 / sizeof(element) (elements per 64-byte chunk),
+ *                element (t, i) at   (i / W) * (block_size * W) + t * W + (i % W)
+ *
+ * i.e. the key tile is cut into head_dim / W chunk rows; chunk row c holds the W elements
+ * [c*W, c*W + W) of slot 0, then of slot 1, ... of slot block_size-1. At block_size 16 a chunk
+ * row is 1 KiB, so one 64-lane wavefront loading 16 bytes per lane reads a whole chunk row in one
+ * fully coalesced instruction, and each group of four lanes holds 64 contiguous bytes of one
+ * token. A tile is 4 KiB in every supported configuration with 256-byte token rows
+ * (head_dim 128 at 16-bit, head_dim 64 at 32-bit).
+ *
+ * Supported: dtype PA_F32 / PA_F16 / PA_BF16 (query, new keys/values, pools and output share
+ * it), head_dim 64 or 128, block_size 16.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
+  PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim or block_size the kernels are not built for */
+  PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned (int arrays: 4-byte) */
+  PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_decode_workspace_bytes() */
+  PA_ERR_LAUNCH = 6,      /* the HIP runtime reported an error when launching */
+} pa_status;
+
+/* Shape of both pools. */
+typedef struct {
+  int32_t dtype;        /* pa_dtype of every element in both pools */
+  int32_t num_blocks;   /* NB: physical blocks per pool */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d */
+  int32_t block_size;   /* B: token slots per block */
+} pa_cache_desc;
+
+/*
+ * pa_reshape_and_cache — write new tokens' keys and values into their cache slots.
+ * ([blog] §2: a token goes into the free slot of its sequence's last block; [anal] §2 and
+ *  "핵심 개념": blocks are attached on demand through the block table.)
+ *
+ * For token n in [0, num_tokens): sequence s = token_seq[n], position p = token_pos[n].
+ * p < 0 skips the token. Otherwise its slot is
+ *     block_tables[s * max_blocks_per_seq + p / B] * B + p % B
+ * and key[n][h][:] / value[n][h][:] are copied bit for bit into the key / value pool at
+ * (slot / B, h, slot % B) for every KV head h.
+ *
+ *   key_cache, value_cache  device, pools in the layout above (written in place)
+ *   key, value              device, [num_tokens][Hkv][d], c->dtype, contiguous
+ *   block_tables            device int32 [num_seqs][max_blocks_per_seq], row-major
+ *   token_seq, token_pos    device int32 [num_tokens]
+ *   num_tokens = 0          returns PA_OK without launching
+ * Caller contract (not checked on the device beyond clamping): distinct tokens map to distinct
+ * slots; block ids in [0, NB). A token whose sequence is outside [0, num_seqs) or whose position
+ * is at or past max_blocks_per_seq * B is skipped; a block id outside [0, NB) is clamped into
+ * range (no fault, but the write lands in the wrong block).
+ */
+pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* value_cache,
+                               const void* key, const void* value, const int32_t* block_tables,
+                               int32_t num_seqs, int32_t max_blocks_per_seq,
+                               const int32_t* token_seq, const int32_t* token_pos,
+                               int32_t num_tokens, void* stream);
+
+/*
+ * pa_decode_workspace_bytes — bytes of device workspace pa_decode needs for these sizes.
+ * partition_size 0 means the library's choice (the same one pa_decode makes). Returns 0 when
+ * no workspace is needed (every context fits one partition) and (size_t)-1 for invalid sizes.
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode — single-query (decode) attention of every sequence over its paged KV cache.
+ * ([wiki] dense and block forms; [anal] §3 block-wise kernel and lookup pseudocode.)
+ *
+ * For sequence s with n = context_lens[s] tokens and query head h (KV head g = h / G with
+ * G = num_q_heads / Hkv): token t in [0, n) is at physical block block_tables[s][t / B],
+ * slot t % B;
+ *     z_t = scale * dot(query[s][h], K_t),   out[s][h] = sum_t softmax(z)_t * V_t.
+ * Slots at or past n in the last block and table entries past ceil(n / B) are never read.
+ * n = 0 writes zeros. Accumulation is fp32; out is rounded to c->dtype (nearest even).
+ *
+ * Contexts longer than one partition are split into partitions of partition_size tokens
+ * (a multiple of B, at most PA_MAX_PARTITION_TOKENS; 0 = library choice). Each partition keeps
+ * its softmax state (running max m, sum l, unnormalised output) in the workspace, and a second
+ * kernel merges the states of each (sequence, head) with the usual max-rescaling.
+ *
+ *   key_cache, value_cache  device pools (layout above), read only
+ *   out                     device [num_seqs][num_q_heads][d], c->dtype
+ *   query                   device [num_seqs][num_q_heads][d], c->dtype
+ *   block_tables            device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens            device int32 [num_seqs]
+ *   scale                   softmax scale (1/sqrt(d) in the usual case)
+ *   max_context_len         host-side upper bound of context_lens (sizes the grid; no
+ *                           device-to-host copy is made); must be <= max_blocks_per_seq * B.
+ *                           A context above it is truncated to it.
+ *   workspace               device, >= pa_decode_workspace_bytes(...) bytes, 256-B aligned
+ *                           (may be NULL when that is 0); contents need no initialisation.
+ * Errors: checked on the host before any HIP call (PA_ERR_NULL / SHAPE / UNSUPPORTED / ALIGN /
+ * WORKSPACE); a failed launch gives PA_ERR_LAUNCH. num_seqs = 0 returns PA_OK. A block id
+ * outside [0, NB) is clamped into range (no fault, but the result is then meaningless).
+ */
+pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
+                    void* out, const void* query, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, int32_t max_context_len,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * The two stages pa_decode launches, exported separately (same arguments, same checks) so a
+ * caller can time or interleave them: pa_decode_attention runs the per-partition attention
+ * kernel (writing out directly for sequences that fit one partition, partition states
+ * otherwise); pa_decode_reduce merges the partition states into out. pa_decode_reduce launches
+ * nothing when every context fits one partition.
+ */
+pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,
+                              const void* value_cache, void* out, const void* query,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              float scale, int32_t max_context_len, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
+                           const void* value_cache, void* out, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, int32_t max_context_len, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_copy_blocks — duplicate whole physical blocks (copy-on-write).
+ * ([anal] §4 and [dev]: a sharer about to write into a block whose reference count exceeds one
+ *  gets a fresh block holding a copy of the old contents; [blog] ②.)
+ *
+ * For each pair k: block src_dst[2k] is copied to block src_dst[2k+1] in both pools: every KV
+ * head and every slot, bit for bit.
+ *   src_dst   device int32 [num_pairs][2]
+ *   num_pairs = 0 returns PA_OK without launching
+ * Caller contract: destination ids are distinct and none is also a source in the same call
+ * (otherwise the copies race). A pair with an id outside [0, NB) is skipped.
+ */
+pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,
+                         const int32_t* src_dst, int32_t num_pairs, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* pa_status_string(pa_status s);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

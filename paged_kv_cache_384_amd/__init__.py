@@ -1,0 +1,242 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libpa.so`` (declared in ``include/pa.h``). The
+functions keep the C names and only marshal arguments: torch tensors become device pointers,
+the current torch stream becomes the HIP stream. Every step of the computation runs in the HIP
+kernels; there is no fallback. If the library is not built, the first call raises.
+
+    pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token_seq, token_pos)
+    pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+              max_context_len, partition_size=0, workspace=None)
+    pa_copy_blocks(key_cache, value_cache, src_dst)
+
+Pools are tensors of shape [num_blocks, num_kv_heads, block_size * head_dim] in the element
+dtype; the order of elements inside each (block, head) tile is the library's (see pa.h).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
+    "pa_decode_reduce", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
+    "pa_abi_version", "ABI_VERSION", "DTYPE_CODES", "EXPORTED_SYMBOLS",
+]
+
+ABI_VERSION = 1
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpa.so")
+
+EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
+                    "pa_decode_attention", "pa_decode_reduce", "pa_copy_blocks",
+                    "pa_status_string", "pa_abi_version"]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({pa_status_string(status)})")
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_desc_p = ctypes.POINTER(CacheDesc)
+_DECODE_ARGS = [_desc_p, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _i32,
+                _i32, _vp, ctypes.c_size_t, _vp]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it first (python -m paged_kv_cache_384_amd._build"
+                " or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(library_path)
+        L.pa_reshape_and_cache.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
+                                           _i32, _vp]
+        L.pa_reshape_and_cache.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [_desc_p, _i32, _i32, _i32, _i32]
+        L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
+            getattr(L, name).argtypes = _DECODE_ARGS
+            getattr(L, name).restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [_desc_p, _vp, _vp, _vp, _i32, _vp]
+        L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_abi_version.argtypes = []
+        L.pa_abi_version.restype = ctypes.c_int32
+        if L.pa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libpa ABI {L.pa_abi_version()} != binding ABI {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def pa_abi_version() -> int:
+    return int(lib().pa_abi_version())
+
+
+# ---- marshalling helpers ------------------------------------------------------------------
+
+def _dtype_name(t) -> str:
+    import torch
+    names = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported element dtype {t.dtype}")
+    return names[t.dtype]
+
+
+def _dev(t, what, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    return _vp(t.data_ptr()) if t.numel() else _vp(0)
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _desc(key_cache, head_dim, block_size) -> CacheDesc:
+    if key_cache.dim() != 3 or key_cache.shape[2] != block_size * head_dim:
+        raise ValueError("pools must be [num_blocks, num_kv_heads, block_size * head_dim]")
+    return CacheDesc(DTYPE_CODES[_dtype_name(key_cache)], key_cache.shape[0], key_cache.shape[1],
+                     head_dim, block_size)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PaError(status, where)
+
+
+# ---- the calls ----------------------------------------------------------------------------
+
+def pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token_seq, token_pos,
+                         *, block_size: int = 16, stream=None) -> None:
+    """Write key[n] / value[n] ([T, Hkv, d]) into the slot of (token_seq[n], token_pos[n])."""
+    import torch
+    head_dim = key.shape[-1]
+    d = _desc(key_cache, head_dim, block_size)
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key and value pools differ in shape or dtype")
+    T = token_seq.numel()
+    if tuple(key.shape) != (T, d.num_kv_heads, head_dim) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim]")
+    if token_pos.numel() != T or block_tables.dim() != 2:
+        raise ValueError("token_pos must match token_seq; block_tables must be 2-D")
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(key, "key", key_cache.dtype), _dev(value, "value", key_cache.dtype),
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[0],
+            block_tables.shape[1], _dev(token_seq, "token_seq", torch.int32),
+            _dev(token_pos, "token_pos", torch.int32), token_seq.numel(),
+            _stream(key_cache, stream))
+    _check(lib().pa_reshape_and_cache(*args), "pa_reshape_and_cache")
+
+
+def pa_decode_workspace_bytes(key_cache, num_seqs: int, num_q_heads: int, head_dim: int,
+                              max_context_len: int, partition_size: int = 0,
+                              block_size: int = 16) -> int:
+    d = _desc(key_cache, head_dim, block_size)
+    n = lib().pa_decode_workspace_bytes(ctypes.byref(d), num_seqs, num_q_heads, max_context_len,
+                                        partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PaError(2, "pa_decode_workspace_bytes")
+    return int(n)
+
+
+def _decode_call(fn_name, out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, partition_size, workspace, block_size, stream):
+    import torch
+    S, Hq, head_dim = query.shape
+    d = _desc(key_cache, head_dim, block_size)
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query in shape and dtype")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key and value pools differ in shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]; context_lens [num_seqs]")
+    need = pa_decode_workspace_bytes(key_cache, S, Hq, head_dim, max_context_len, partition_size,
+                                     block_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else _vp(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache", query.dtype),
+            _dev(value_cache, "value_cache", query.dtype), _dev(out, "out"),
+            _dev(query, "query"), _dev(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S, Hq,
+            float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+            _stream(query, stream))
+    _check(getattr(lib(), fn_name)(*args), fn_name)
+    return workspace
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+              max_context_len, partition_size: int = 0, workspace=None, *, block_size: int = 16,
+              stream=None):
+    """out[s, h] = attention of query[s, h] over sequence s's paged cache (both stages).
+
+    Returns the workspace used (allocated with torch when none is given and one is needed).
+    """
+    return _decode_call("pa_decode", out, query, key_cache, value_cache, block_tables,
+                        context_lens, scale, max_context_len, partition_size, workspace,
+                        block_size, stream)
+
+
+def pa_decode_attention(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size: int = 0, workspace=None, *,
+                        block_size: int = 16, stream=None):
+    """First stage of pa_decode only (per-partition attention)."""
+    return _decode_call("pa_decode_attention", out, query, key_cache, value_cache, block_tables,
+                        context_lens, scale, max_context_len, partition_size, workspace,
+                        block_size, stream)
+
+
+def pa_decode_reduce(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     max_context_len, partition_size: int = 0, workspace=None, *,
+                     block_size: int = 16, stream=None):
+    """Second stage of pa_decode only (merge of partition states)."""
+    return _decode_call("pa_decode_reduce", out, query, key_cache, value_cache, block_tables,
+                        context_lens, scale, max_context_len, partition_size, workspace,
+                        block_size, stream)
+
+
+def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int = 16,
+                   stream=None) -> None:
+    """Copy block src_dst[k, 0] onto block src_dst[k, 1] in both pools."""
+    import torch
+    d = _desc(key_cache, head_dim, block_size)
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key and value pools differ in shape")
+    if src_dst.numel() % 2:
+        raise ValueError("src_dst must hold (src, dst) pairs")
+    pairs = src_dst.reshape(-1, 2) if src_dst.numel() else src_dst
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache", key_cache.dtype),
+            _dev(src_dst, "src_dst", torch.int32), pairs.shape[0] if src_dst.numel() else 0,
+            _stream(key_cache, stream))
+    _check(lib().pa_copy_blocks(*args), "pa_copy_blocks")

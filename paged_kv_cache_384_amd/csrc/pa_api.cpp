@@ -1,0 +1,255 @@
+// C ABI of the paged decode library: argument checks on the host, partition choice, dispatch.
+// Every check runs before any HIP call; the only HIP calls are the launches and
+// hipGetLastError. Nothing is allocated.
+#include <stdint.h>
+
+#include "../../include/pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+using pa::DType;
+
+constexpr int kStageAttention = 1;
+constexpr int kStageReduce = 2;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_size(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+pa_status check_desc(const pa_cache_desc* c) {
+  if (c == nullptr) return PA_ERR_NULL;
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (c->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int64_t tile_bytes(const pa_cache_desc* c) {
+  return static_cast<int64_t>(c->block_size) * c->head_dim * elem_size(c->dtype);
+}
+
+// Partition size when the caller passes 0. One partition when the longest context fits in
+// 512 tokens; otherwise 512-token partitions (32 blocks: eight per wavefront), which keeps
+// every workgroup's key/value stream long enough to amortise its setup while giving the
+// launch enough independent workgroups for 256 CUs.
+int32_t choose_partition(int32_t max_context_len, int32_t requested) {
+  if (requested > 0) return requested;
+  constexpr int32_t kDefault = 512;
+  if (max_context_len <= kDefault) {
+    const int32_t p = (max_context_len + pa::kBlockSize - 1) / pa::kBlockSize * pa::kBlockSize;
+    return p < pa::kBlockSize ? pa::kBlockSize : p;
+  }
+  return kDefault;
+}
+
+struct DecodePlan {
+  int32_t part_tokens;
+  int32_t num_parts;
+  int32_t heads_per_wg;
+  size_t workspace_bytes;
+};
+
+pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, int32_t partition_size, DecodePlan* plan) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (max_context_len < 0) return PA_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % c->block_size != 0 ||
+      partition_size > pa::kMaxPartitionTokens)
+    return PA_ERR_SHAPE;
+  const int32_t part = choose_partition(max_context_len, partition_size);
+  const int32_t np = max_context_len <= part ? 1 : (max_context_len + part - 1) / part;
+  const int32_t group = num_q_heads / c->num_kv_heads;
+  const int32_t nh = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  const int64_t wgs = static_cast<int64_t>(c->num_kv_heads) * num_seqs * (group / nh) * np;
+  if (wgs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  plan->part_tokens = part;
+  plan->num_parts = np;
+  plan->heads_per_wg = nh;
+  plan->workspace_bytes =
+      np > 1 ? static_cast<size_t>(num_seqs) * num_q_heads * np * (c->head_dim + 2) * sizeof(float)
+             : 0;
+  return PA_OK;
+}
+
+pa_status decode_impl(int stages, const pa_cache_desc* c, const void* key_cache,
+                      const void* value_cache, void* out, const void* query,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      float scale, int32_t max_context_len, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  pa_status st = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !out || !query || !block_tables || !context_lens)
+    return PA_ERR_NULL;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(out, 16) ||
+      !aligned(query, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  }
+
+  pa::DecodeArgs a;
+  a.k_pool = static_cast<const uint8_t*>(key_cache);
+  a.v_pool = static_cast<const uint8_t*>(value_cache);
+  a.out = static_cast<uint8_t*>(out);
+  a.query = static_cast<const uint8_t*>(query);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const int64_t states = static_cast<int64_t>(num_seqs) * num_q_heads * plan.num_parts;
+  float* ws = static_cast<float*>(workspace);
+  a.ws_acc = plan.workspace_bytes ? ws : nullptr;
+  a.ws_m = plan.workspace_bytes ? ws + states * c->head_dim : nullptr;
+  a.ws_l = plan.workspace_bytes ? ws + states * (c->head_dim + 1) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.group = num_q_heads / c->num_kv_heads;
+  a.heads_per_wg = plan.heads_per_wg;
+  a.head_groups = a.group / plan.heads_per_wg;
+  a.part_tokens = plan.part_tokens;
+  a.num_parts = plan.num_parts;
+  a.max_ctx = max_context_len;
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+
+  const DType dt = static_cast<DType>(c->dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (stages & kStageAttention) {
+    if (pa::launch_decode_attention(dt, c->head_dim, a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (stages & kStageReduce) {
+    if (pa::launch_decode_reduce(dt, c->head_dim, a, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* value_cache,
+                               const void* key, const void* value, const int32_t* block_tables,
+                               int32_t num_seqs, int32_t max_blocks_per_seq,
+                               const int32_t* token_seq, const int32_t* token_pos,
+                               int32_t num_tokens, void* stream) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!key_cache || !value_cache || !key || !value || !block_tables || !token_seq || !token_pos)
+    return PA_ERR_NULL;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key, 16) ||
+      !aligned(value, 16) || !aligned(block_tables, 4) || !aligned(token_seq, 4) ||
+      !aligned(token_pos, 4))
+    return PA_ERR_ALIGN;
+  pa::CacheWriteArgs a;
+  a.k_pool = static_cast<uint8_t*>(key_cache);
+  a.v_pool = static_cast<uint8_t*>(value_cache);
+  a.key = static_cast<const uint8_t*>(key);
+  a.value = static_cast<const uint8_t*>(value);
+  a.block_tables = block_tables;
+  a.token_seq = token_seq;
+  a.token_pos = token_pos;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = c->num_blocks;
+  a.num_kv_heads = c->num_kv_heads;
+  if (pa::launch_reshape_and_cache(static_cast<DType>(c->dtype), c->head_dim, a,
+                                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size) {
+  DecodePlan plan;
+  if (plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size, &plan) != PA_OK)
+    return static_cast<size_t>(-1);
+  return plan.workspace_bytes;
+}
+
+pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
+                    void* out, const void* query, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, int32_t max_context_len,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_impl(kStageAttention | kStageReduce, c, key_cache, value_cache, out, query,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                     max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,
+                              const void* value_cache, void* out, const void* query,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              float scale, int32_t max_context_len, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kStageAttention, c, key_cache, value_cache, out, query, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                     max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
+                           const void* value_cache, void* out, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, int32_t max_context_len, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kStageReduce, c, key_cache, value_cache, out, query, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                     max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,
+                         const int32_t* src_dst, int32_t num_pairs, void* stream) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !src_dst) return PA_ERR_NULL;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(src_dst, 4))
+    return PA_ERR_ALIGN;
+  pa::CopyArgs a;
+  a.k_pool = static_cast<uint8_t*>(key_cache);
+  a.v_pool = static_cast<uint8_t*>(value_cache);
+  a.pairs = src_dst;
+  a.num_pairs = num_pairs;
+  a.num_blocks = c->num_blocks;
+  a.block_bytes = tile_bytes(c) * c->num_kv_heads;
+  const int64_t chunks = (a.block_bytes / 16 + 2047) / 2048;
+  if (chunks * num_pairs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or block_size";
+    case PA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for data, 4 for int32 arrays)";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes()";
+    case PA_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+  }
+  return "unknown status";
+}
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Cache-side kernels: writing new tokens into their slots and copying whole blocks.
+//
+// Sources (page title, section):
+//   "PagedAttention 논문 쉽게 읽기" (iplexlaw.co.kr), §2: a new token's key/value goes into the free
+//   slot of its sequence's last block, found through the block table; ②: a shared block about
+//   to be written is copied first.
+//   "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net), §4 copy-on-write;
+//   "추론 엔진에서의 메모리 가상화" (molayo1419.me), copy-on-write: fresh block, copy, remap.
+#include "pa_device.h"
+
+namespace pa {
+
+// One workgroup per new token. Each thread moves 16-byte pieces: piece q of KV head h holds
+// elements [q*Epp, q*Epp + Epp) of that head's vector. In the value tile it goes to row `slot`,
+// byte q*16; in the key tile to chunk row q/4 (64-byte chunks = 4 pieces), slot `slot`, byte
+// (q%4)*16 of that slot's 64-byte segment.
+template <DType dt, int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
+  using G = TileGeom<dt, D>;
+  const int n = blockIdx.x;
+  const int s = a.token_seq[n];
+  const int pos = a.token_pos[n];
+  if (pos < 0 || pos >= a.max_blocks * kBlockSize || s < 0 || s >= a.num_seqs) return;
+  int blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + pos / kBlockSize];
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  const int slot = pos % kBlockSize;
+  constexpr int kPieces = G::kPiecesPerRow;
+  const int total = a.num_kv_heads * kPieces;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int h = i / kPieces;
+    const int q = i % kPieces;
+    const int64_t src = (static_cast<int64_t>(n) * a.num_kv_heads + h) * G::kRowBytes + q * 16;
+    const int64_t tile = (static_cast<int64_t>(blk) * a.num_kv_heads + h) * G::kTileBytes;
+    const u32x4 kv = load16(a.key + src);
+    const u32x4 vv = load16(a.value + src);
+    store16(a.k_pool + tile + (q >> 2) * (kBlockSize * 64) + slot * 64 + (q & 3) * 16, kv);
+    store16(a.v_pool + tile + slot * G::kRowBytes + q * 16, vv);
+  }
+}
+
+// Grid: num_pairs * chunks workgroups; each copies its chunk of one block in both pools.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, int chunks,
+                                                          int64_t chunk_pieces) {
+  const int pair = blockIdx.x / chunks;
+  const int chunk = blockIdx.x % chunks;
+  const int src = a.pairs[2 * pair];
+  const int dst = a.pairs[2 * pair + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  const int64_t pieces = a.block_bytes / 16;
+  const int64_t p0 = chunk * chunk_pieces;
+  const int64_t p1 = p0 + chunk_pieces < pieces ? p0 + chunk_pieces : pieces;
+  const int64_t so = static_cast<int64_t>(src) * a.block_bytes;
+  const int64_t d0 = static_cast<int64_t>(dst) * a.block_bytes;
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    store16(a.k_pool + d0 + p * 16, load16(a.k_pool + so + p * 16));
+    store16(a.v_pool + d0 + p * 16, load16(a.v_pool + so + p * 16));
+  }
+}
+
+template <DType dt, int D>
+static hipError_t launch_rc(const CacheWriteArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((reshape_and_cache_kernel<dt, D>), dim3(a.num_tokens), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(DType dt, int head_dim, const CacheWriteArgs& a,
+                                    hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  switch (dt) {
+    case DType::F32: return head_dim == 64 ? launch_rc<DType::F32, 64>(a, stream)
+                                           : launch_rc<DType::F32, 128>(a, stream);
+    case DType::F16: return head_dim == 64 ? launch_rc<DType::F16, 64>(a, stream)
+                                           : launch_rc<DType::F16, 128>(a, stream);
+    case DType::BF16: return head_dim == 64 ? launch_rc<DType::BF16, 64>(a, stream)
+                                            : launch_rc<DType::BF16, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
+  if (a.num_pairs == 0) return hipSuccess;
+  // 256 threads x 8 pieces of 16 B = 32 KiB of each pool per workgroup
+  const int64_t chunk_pieces = 256 * 8;
+  const int64_t pieces = a.block_bytes / 16;
+  const int chunks = static_cast<int>((pieces + chunk_pieces - 1) / chunk_pieces);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(a.num_pairs) * chunks),
+                     dim3(256), 0, stream, a, chunks, chunk_pieces);
+  return hipGetLastError();
+}
+
+}  // namespace pa

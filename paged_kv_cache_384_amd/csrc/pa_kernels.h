@@ -1,0 +1,73 @@
+// Internal interface between the C ABI (pa_api.cpp) and the HIP kernels. Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+constexpr int kBlockSize = 16;         // token slots per KV block
+constexpr int kMaxPartitionTokens = 2048;
+constexpr int kMaxPartitionBlocks = kMaxPartitionTokens / kBlockSize;
+constexpr int kDecodeThreads = 256;    // four 64-lane wavefronts per attention workgroup
+
+struct CacheWriteArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const uint8_t* key;
+  const uint8_t* value;
+  const int32_t* block_tables;
+  const int32_t* token_seq;
+  const int32_t* token_pos;
+  int32_t num_tokens;
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+};
+
+struct CopyArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const int32_t* pairs;
+  int32_t num_pairs;
+  int32_t num_blocks;
+  int64_t block_bytes;  // bytes of one physical block in one pool (all KV heads)
+};
+
+// One launch of the attention stage covers every (KV head, sequence, head group, partition).
+struct DecodeArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  uint8_t* out;
+  const uint8_t* query;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_m;    // [S][Hq][NP] running max (log2 domain)
+  float* ws_l;    // [S][Hq][NP] sum of exp2(z - m)
+  float* ws_acc;  // [S][Hq][NP][D] unnormalised output
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t group;        // query heads per KV head
+  int32_t heads_per_wg; // query heads one workgroup handles (1, 2 or 4)
+  int32_t head_groups;  // group / heads_per_wg
+  int32_t part_tokens;  // partition size in tokens (multiple of 16)
+  int32_t num_parts;    // partitions of the longest context
+  int32_t max_ctx;
+  float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
+};
+
+// Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).
+hipError_t launch_reshape_and_cache(DType dt, int head_dim, const CacheWriteArgs& a,
+                                    hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
+                                   hipStream_t stream);
+hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

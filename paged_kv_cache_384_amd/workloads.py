@@ -55,6 +55,7 @@ class DecodeConfig:
     """One synthetic decode workload.
 
     ``ctx`` names the context-length distribution:
+      ("fixed", (n_0, n_1, ...))              the given lengths, one per sequence
       ("uniform", lo, hi)                     integers, both ends inclusive
       ("lognormal", median, sigma, lo, hi)    round(exp(N(ln median, sigma^2))), clipped
       ("shared_prefix", prompt, lo, hi, n)    ``num_seqs // n`` prompts of ``prompt`` tokens,
@@ -93,6 +94,8 @@ class DecodeConfig:
     def max_ctx_bound(self) -> int:
         """Largest context the distribution can produce (sizes the block-table width)."""
         kind = self.ctx[0]
+        if kind == "fixed":
+            return max(int(n) for n in self.ctx[1]) if len(self.ctx[1]) else 0
         if kind == "uniform":
             return int(self.ctx[2])
         if kind == "lognormal":
@@ -265,6 +268,11 @@ class DecodeBatch:
 
 def _draw_context_lens(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
     kind = cfg.ctx[0]
+    if kind == "fixed":
+        lens = np.asarray(cfg.ctx[1], dtype=np.int64)
+        if lens.shape != (cfg.num_seqs,):
+            raise ValueError("one fixed length per sequence")
+        return lens
     if kind == "uniform":
         lo, hi = cfg.ctx[1], cfg.ctx[2]
         return rng.integers(lo, hi + 1, size=cfg.num_seqs).astype(np.int64)
@@ -320,7 +328,7 @@ def build_batch(cfg: DecodeConfig) -> DecodeBatch:
             bm.append_tokens(s, int(c))
             seqs.append(s)
     S = cfg.num_seqs
-    maxb = -(-cfg.max_ctx_bound // B)
+    maxb = max(1, -(-cfg.max_ctx_bound // B))
     tables = np.full((S, maxb), poison, dtype=np.int32)
     for i, s in enumerate(seqs):
         t = bm.tables[s]
