@@ -5,41 +5,151 @@
 //   and the same result written block by block over K_j, V_j.
 //   "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net), §3 and its block-table
 //   lookup pseudocode: per logical block, look up the physical block, score its keys, fold the
-//   scores and values into softmax partial sums; the result equals ordinary attention.
+//   scores and values into running softmax sums (running max, running denominator, running
+//   output, one division at the end); the result equals ordinary attention.
 //
 // Work decomposition (gfx950): one 256-thread workgroup (four wavefronts) per
-// (KV head, sequence, query-head group, context partition). Inside a workgroup:
-//   1. the partition's block-table slice is staged in LDS;
-//   2. keys: each wavefront takes every fourth block; per block it issues kLoads 16-byte loads
-//      per lane, each reading one whole 1 KiB key chunk row, so lane l holds 64 contiguous
-//      bytes of token l/4 per row; dot2 instructions against the query piece the lane keeps in
-//      registers, then a two-step DPP quad sum, give every token's score (base-2 domain);
-//      scores go to LDS;
-//   3. the partition maximum and exp2(score - max) are formed once per token in LDS;
-//   4. values: each wavefront again takes every fourth block; lane l reads 16-byte pieces of
-//      token rows and accumulates weight * value for its kEpp columns in fp32;
-//   5. lanes holding the same columns are summed across the wavefront, then across the four
-//      wavefronts through LDS; the workgroup writes the normalised output (single partition)
-//      or its partition state (max, sum, unnormalised output) for the merge kernel.
-// Only the last block of a partition can hold slots past the context end; those are masked
-// with a select (score -inf, value 0) so stale or NaN contents never enter the result.
+// (KV head, sequence, query-head group, context partition). The partition's block-table slice
+// is staged in LDS; wavefront w then streams blocks w, w+4, w+8, ... of the partition in a
+// single pass over keys and values:
+//   * keys: kLoads 16-byte loads per lane, each reading one whole 1 KiB key chunk row, so lane l
+//     holds 64 contiguous bytes of token l/4 per row; dot2 instructions against the query piece
+//     the lane keeps in registers and a two-step DPP quad sum give every token's score in the
+//     base-2 domain (scale * log2 e folded in);
+//   * running softmax, one state per wavefront: the maximum m is the same in every lane and is
+//     raised only when some score exceeds it by more than kRescaleSlack (a ballot, so the
+//     rescale of the running sums is a rare, uniform branch); weights are 2^(score - m) <=
+//     2^kRescaleSlack, and the division at the end cancels the choice of m exactly;
+//   * values: lane l reads 16-byte pieces of kLoads value rows and accumulates weight * value
+//     for its kEpp columns in fp32; the weights of those rows are moved from the lanes that
+//     scored them with DPP row broadcasts (or ds_bpermute for other tile shapes);
+//   * the next block's keys are requested as soon as the scores are formed and its values as
+//     soon as the weighted sum is done, so a wavefront always has a block's loads in flight.
+// The four wavefront states are merged through LDS with the usual max-rescaling; the
+// workgroup writes the normalised output (one partition) or its partition state (max, sum,
+// unnormalised output) for the merge kernel. Only the last block of a partition can hold slots
+// past the context end; those are masked with selects (score -inf, value 0) so stale or NaN
+// contents never enter the result.
+#include <utility>
+
 #include "pa_device.h"
 
 namespace pa {
 
-template <DType dt, int D, int NH, int UNROLL>
+// A wavefront's running maximum is raised only when a score exceeds it by more than this many
+// powers of two; weights therefore stay <= 2^8, far from fp32 overflow.
+constexpr float kRescaleSlack = 8.0f;
+
+// Weight of value row vrow0 + I for a lane whose value rows start at vrow0: that row's score
+// sits in lanes 4 * (vrow0 + I) .. +3.
+template <int kPiecesPerRow, int kLoads>
+struct RowWeights {
+  template <int... I>
+  __device__ static __forceinline__ void run(float p, int lane, float* w,
+                                             std::integer_sequence<int, I...>) {
+    if constexpr (kPiecesPerRow == 16 && kLoads == 4) {
+      // value rows 4*(l/16) + I are scored in lanes 16*(l/16) + 4*I: lane 4*I of the lane's own
+      // row of 16, which DPP row_newbcast broadcasts within each row
+      ((w[I] = bits_f32(__builtin_amdgcn_update_dpp(0u, f32_bits(p), 0x150 + 4 * I, 0xF, 0xF,
+                                                    false))), ...);
+    } else {
+      const int src = ((lane / kPiecesPerRow) * kLoads) * 16;  // byte address of lane 4*vrow0
+      ((w[I] = bits_f32(__builtin_amdgcn_ds_bpermute(src + 16 * I, static_cast<int>(f32_bits(p))))),
+       ...);
+    }
+  }
+};
+
+// One block of one wavefront's stream: scores, running-softmax update, weighted values.
+// kPrefetch: the block is full and the next one (at byte offset offn) is loaded into the key
+// and value registers as soon as each is consumed. Otherwise the block may be the partition's
+// last, so slots at or past len are masked, and nothing is loaded.
+template <DType dt, int D, int NH, bool kPrefetch>
+struct BlockStep {
+  using G = TileGeom<dt, D>;
+  static constexpr int kLoads = G::kLoads;
+  static constexpr int kEpp = G::kEpp;
+  static constexpr int kPiecesPerRow = G::kPiecesPerRow;
+
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  int64_t tile_stride;
+  float scale_log2;
+  int lane;
+  int vrow0;
+  int len;
+
+  __device__ __forceinline__ void run(int j, int64_t offn, const u32x4 (&qv)[NH][kLoads],
+                                      u32x4 (&kb)[kLoads], u32x4 (&vb)[kLoads], float (&m)[NH],
+                                      float (&lsum)[NH], float (&acc)[NH][kEpp]) const {
+    float sc[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      float d = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) d = Dot16<dt>::run(kb[c], qv[hh][c], d);
+      sc[hh] = quad_sum(d) * scale_log2;
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) kb[c] = load16(kbase + offn + c * 1024);
+    } else {
+      const bool valid = j * kBlockSize + (lane >> 2) < len;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) sc[hh] = valid ? sc[hh] : -INFINITY;
+    }
+
+    float pw[NH][kLoads];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      if (__builtin_amdgcn_ballot_w64(sc[hh] > m[hh] + kRescaleSlack) != 0) {
+        const float mn = wave_max(sc[hh]);
+        const float c = exp2_fast(m[hh] - mn);
+        lsum[hh] *= c;
+#pragma unroll
+        for (int e = 0; e < kEpp; ++e) acc[hh][e] *= c;
+        m[hh] = mn;
+      }
+      const float p = exp2_fast(sc[hh] - m[hh]);
+      lsum[hh] += p;
+      RowWeights<kPiecesPerRow, kLoads>::run(p, lane, pw[hh],
+                                             std::make_integer_sequence<int, kLoads>{});
+    }
+
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      float v[kEpp];
+      Widen<dt>::run(vb[i], v);
+      if constexpr (!kPrefetch) {
+        if (j * kBlockSize + vrow0 + i >= len) {
+#pragma unroll
+          for (int e = 0; e < kEpp; ++e) v[e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(pw[hh][i], v[e], acc[hh][e]);
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) vb[i] = load16(vbase + offn + i * G::kRowBytes);
+    }
+  }
+};
+
+template <DType dt, int D, int NH>
 __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
   using G = TileGeom<dt, D>;
   constexpr int kLoads = G::kLoads;
   constexpr int kEpp = G::kEpp;
   constexpr int kPiecesPerRow = G::kPiecesPerRow;
-  constexpr int kRowsPerLoad = G::kRowsPerLoad;
   constexpr int kWaves = kDecodeThreads / 64;
 
-  extern __shared__ float smem[];                 // scores [NH][part_tokens], then reduction
   __shared__ int bt_s[kMaxPartitionBlocks];
-  __shared__ float wmax_s[kWaves][NH];
-  __shared__ float wsum_s[kWaves][NH];
+  __shared__ float red_s[kWaves][NH][D];
+  __shared__ float m_s[kWaves][NH];
+  __shared__ float l_s[kWaves][NH];
 
   // ---- which work item -------------------------------------------------------------------
   int r = xcd_logical_index();
@@ -74,9 +184,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
 
   // ---- stage the block-table slice and the query pieces -------------------------------------
   {
-    const int32_t* row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
+    const int32_t* row =
+        a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
     for (int j = tid; j < nblk; j += kDecodeThreads) {
-      int id = row[j];
+      const int id = row[j];
       bt_s[j] = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
     }
   }
@@ -92,156 +203,70 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   }
   __syncthreads();
 
-  float* sc = smem;                               // [NH][part_tokens]
-  const int64_t head_tiles = a.num_kv_heads;
+  const int64_t tile_stride = static_cast<int64_t>(a.num_kv_heads) * G::kTileBytes;
+  const uint8_t* kbase = a.k_pool + static_cast<int64_t>(kvh) * G::kTileBytes + lane * 16;
+  // value piece i of a lane: row vrow0 + i, bytes [(lane % kPiecesPerRow) * 16, +16)
+  const int vrow0 = (lane / kPiecesPerRow) * kLoads;
+  const uint8_t* vbase = a.v_pool + static_cast<int64_t>(kvh) * G::kTileBytes +
+                         vrow0 * G::kRowBytes + (lane % kPiecesPerRow) * 16;
   const float scale_log2 = a.scale_log2;
 
-  // ---- pass 1: scores --------------------------------------------------------------------
-  float lmax[NH];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) lmax[hh] = -INFINITY;
-  const int tok = lane >> 2;
-  for (int j0 = wave; j0 < nblk; j0 += kWaves * UNROLL) {
-    u32x4 kr[UNROLL][kLoads];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = j0 + kWaves * u;
-      if (j < nblk) {
-        const int phys = __builtin_amdgcn_readfirstlane(bt_s[j]);
-        const uint8_t* tile = a.k_pool + (phys * head_tiles + kvh) * G::kTileBytes;
-#pragma unroll
-        for (int c = 0; c < kLoads; ++c) kr[u][c] = load16(tile + c * 1024 + lane * 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = j0 + kWaves * u;
-      if (j < nblk) {
-        const int t = j * kBlockSize + tok;
-        const bool valid = t < len;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          float d = 0.0f;
-#pragma unroll
-          for (int c = 0; c < kLoads; ++c) d = Dot16<dt>::run(kr[u][c], qv[hh][c], d);
-          d = quad_sum(d);
-          const float z = valid ? d * scale_log2 : -INFINITY;
-          if ((lane & 3) == 0) sc[hh * a.part_tokens + t] = z;
-          lmax[hh] = fmaxf(lmax[hh], z);
-        }
-      }
-    }
-  }
+  float m[NH], lsum[NH], acc[NH][kEpp];
 #pragma unroll
   for (int hh = 0; hh < NH; ++hh) {
-    const float m = wave_max(lmax[hh]);
-    if (lane == 0) wmax_s[wave][hh] = m;
-  }
-  __syncthreads();
-
-  // ---- pass 2: weights exp2(z - max) and their sum ----------------------------------------
-  float M[NH], L[NH];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    float m = wmax_s[0][hh];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, wmax_s[w][hh]);
-    M[hh] = m;
-  }
-  {
-    float lsum[NH];
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) lsum[hh] = 0.0f;
-    for (int t = tid; t < nblk * kBlockSize; t += kDecodeThreads) {
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        const float p = exp2_fast(sc[hh * a.part_tokens + t] - M[hh]);
-        sc[hh * a.part_tokens + t] = p;
-        lsum[hh] += p;
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      const float l = wave_sum(lsum[hh]);
-      if (lane == 0) wsum_s[wave][hh] = l;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) l += wsum_s[w][hh];
-    L[hh] = l;
-  }
-
-  // ---- pass 3: weighted values -----------------------------------------------------------
-  // load i of lane l covers value row (l / PiecesPerRow) * kLoads + i of the block, columns
-  // [(l % PiecesPerRow) * Epp, +Epp): each lane's rows are consecutive, so its weights are one
-  // vector LDS read per head.
-  const int vrow0 = (lane / kPiecesPerRow) * kLoads;
-  const int vbyte = (lane % kPiecesPerRow) * 16;
-  float acc[NH][kEpp];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh)
+    m[hh] = -INFINITY;
+    lsum[hh] = 0.0f;
 #pragma unroll
     for (int e = 0; e < kEpp; ++e) acc[hh][e] = 0.0f;
-
-  for (int j0 = wave; j0 < nblk; j0 += kWaves * UNROLL) {
-    u32x4 vr[UNROLL][kLoads];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = j0 + kWaves * u;
-      if (j < nblk) {
-        const int phys = __builtin_amdgcn_readfirstlane(bt_s[j]);
-        const uint8_t* tile = a.v_pool + (phys * head_tiles + kvh) * G::kTileBytes;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-          vr[u][i] = load16(tile + (vrow0 + i) * G::kRowBytes + vbyte);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = j0 + kWaves * u;
-      if (j < nblk) {
-        const int t0 = j * kBlockSize + vrow0;
-        const bool tail = (j == nblk - 1) && (len % kBlockSize) != 0;
-        float pw[NH][kLoads];
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int i = 0; i < kLoads; ++i) pw[hh][i] = sc[hh * a.part_tokens + t0 + i];
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-          float v[kEpp];
-          Widen<dt>::run(vr[u][i], v);
-          if (tail && t0 + i >= len) {
-#pragma unroll
-            for (int e = 0; e < kEpp; ++e) v[e] = 0.0f;
-          }
-#pragma unroll
-          for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-            for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(pw[hh][i], v[e], acc[hh][e]);
-        }
-      }
-    }
   }
 
-  // ---- combine lanes, then wavefronts ------------------------------------------------------
+  // first block of this wavefront; a wavefront with no block (partitions of fewer than four
+  // blocks) loads the partition's last block and never uses it, so that the loads are issued on
+  // every path and the compiler's wait counts for the loop stay exact
+  u32x4 kb[kLoads], vb[kLoads];
+  int j = wave;
+  {
+    const int64_t off =
+        __builtin_amdgcn_readfirstlane(bt_s[j < nblk ? j : nblk - 1]) * tile_stride;
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh)
+    for (int c = 0; c < kLoads; ++c) kb[c] = load16(kbase + off + c * 1024);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) vb[i] = load16(vbase + off + i * G::kRowBytes);
+  }
+  // every block but the wavefront's last: full blocks, next block's loads always issued (so
+  // the wait counts stay exact); the wavefront's last block may be the partition's partial
+  // one and issues nothing
+  BlockStep<dt, D, NH, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+  for (; j + kWaves < nblk; j += kWaves)
+    full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qv, kb, vb, m,
+             lsum, acc);
+  if (j < nblk) {
+    BlockStep<dt, D, NH, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+    tail.run(j, 0, qv, kb, vb, m, lsum, acc);
+  }
+
+  // ---- combine lanes holding the same columns, then the four wavefronts -------------------
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
 #pragma unroll
     for (int e = 0; e < kEpp; ++e)
 #pragma unroll
       for (int o = kPiecesPerRow; o < 64; o <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
-
-  float* red = smem + NH * a.part_tokens;        // [kWaves][NH][D]
+    // every token's weight was added in its four scoring lanes
+    lsum[hh] = wave_sum(lsum[hh]) * 0.25f;
+  }
   if (lane < kPiecesPerRow) {
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-      for (int e = 0; e < kEpp; ++e) red[(wave * NH + hh) * D + lane * kEpp + e] = acc[hh][e];
+      for (int e = 0; e < kEpp; ++e) red_s[wave][hh][lane * kEpp + e] = acc[hh][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      m_s[wave][hh] = m[hh];
+      l_s[wave][hh] = lsum[hh];
+    }
   }
   __syncthreads();
 
@@ -249,74 +274,95 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   for (int i = tid; i < NH * D; i += kDecodeThreads) {
     const int hh = i / D;
     const int col = i % D;
-    float o = 0.0f;
+    // wave 0 always holds block 0, so the maximum is finite; idle wavefronts (m = -inf,
+    // sums 0) get weight 0
+    float M = m_s[0][hh];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += red[(w * NH + hh) * D + col];
-    float Lh = 0.0f, Mh = 0.0f;
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_s[w][hh]);
+    float o = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NH; ++k) {
-      if (k == hh) { Lh = L[k]; Mh = M[k]; }
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = exp2_fast(m_s[w][hh] - M);
+      o = __builtin_fmaf(c, red_s[w][hh][col], o);
+      L = __builtin_fmaf(c, l_s[w][hh], L);
     }
     if (nparts == 1) {
-      Narrow<dt>::store(a.out + ((sh0 + hh) * D + col) * G::kEsz, o / Lh);
+      Narrow<dt>::store(a.out + ((sh0 + hh) * D + col) * G::kEsz, o / L);
     } else {
       const int64_t st = (sh0 + hh) * a.num_parts + part;
       a.ws_acc[st * D + col] = o;
       if (col == 0) {
-        a.ws_m[st] = Mh;
-        a.ws_l[st] = Lh;
+        a.ws_m[st] = M;
+        a.ws_l[st] = L;
       }
     }
   }
 }
 
-// One 64-lane workgroup per (sequence, query head): merge that pair's partition states.
+// One 256-thread workgroup per (sequence, query head) merges that pair's partition states:
+// thread t owns column t % D of partition group t / D (partitions p = group, group + G, ...),
+// so every thread streams its partitions' values with independent loads; the G groups are
+// summed through LDS.
 template <DType dt, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArgs a) {
   using G = TileGeom<dt, D>;
-  constexpr int kCols = D / 64;
+  constexpr int kGroups = kReduceThreads / D;
+  __shared__ float red_s[kReduceThreads];
+  __shared__ float lred_s[kGroups];
+  __shared__ float wmax_s[kReduceThreads / 64];
+
   const int sh = blockIdx.x;
   const int s = sh / a.num_q_heads;
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;  // written directly by the attention kernel
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const float* m = a.ws_m + static_cast<int64_t>(sh) * a.num_parts;
   const float* l = a.ws_l + static_cast<int64_t>(sh) * a.num_parts;
   const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
+
   float M = -INFINITY;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, m[p]);
+  for (int p = tid; p < np; p += kReduceThreads) M = fmaxf(M, m[p]);
   M = wave_max(M);
-  float L = 0.0f;
-  for (int p = lane; p < np; p += 64) L += l[p] * exp2_fast(m[p] - M);
-  L = wave_sum(L);
-  float o[kCols];
+  if (lane == 0) wmax_s[tid >> 6] = M;
+  __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kCols; ++e) o[e] = 0.0f;
-  for (int p = 0; p < np; ++p) {
+  for (int w = 0; w < kReduceThreads / 64; ++w) M = fmaxf(M, wmax_s[w]);
+
+  const int col = tid % D;
+  const int grp = tid / D;
+  float o = 0.0f, L = 0.0f;
+#pragma unroll 8
+  for (int p = grp; p < np; p += kGroups) {
     const float w = exp2_fast(m[p] - M);
-#pragma unroll
-    for (int e = 0; e < kCols; ++e) o[e] = __builtin_fmaf(w, acc[p * D + lane * kCols + e], o[e]);
+    o = __builtin_fmaf(w, acc[static_cast<int64_t>(p) * D + col], o);
+    L = __builtin_fmaf(w, l[p], L);
   }
-  const float inv = 1.0f / L;
+  red_s[tid] = o;
+  if (col == 0) lred_s[grp] = L;
+  __syncthreads();
+  if (tid < D) {
+    float ot = 0.0f, lt = 0.0f;
 #pragma unroll
-  for (int e = 0; e < kCols; ++e)
-    Narrow<dt>::store(a.out + (static_cast<int64_t>(sh) * D + lane * kCols + e) * G::kEsz,
-                      o[e] * inv);
+    for (int g = 0; g < kGroups; ++g) {
+      ot += red_s[g * D + tid];
+      lt += lred_s[g];
+    }
+    Narrow<dt>::store(a.out + (static_cast<int64_t>(sh) * D + tid) * G::kEsz, ot / lt);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
-constexpr int kUnroll = 2;
-
 template <DType dt, int D, int NH>
 static hipError_t launch_attn(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t n = static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.head_groups * a.num_parts;
-  const size_t lds = (static_cast<size_t>(NH) * a.part_tokens + 4 * NH * D) * sizeof(float);
-  hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, kUnroll>), dim3(static_cast<unsigned>(n)),
-                     dim3(kDecodeThreads), lds, stream, a);
+  const int64_t n =
+      static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.head_groups * a.num_parts;
+  hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH>), dim3(static_cast<unsigned>(n)),
+                     dim3(kDecodeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -345,8 +391,8 @@ hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
 template <DType dt, int D>
 static hipError_t launch_red(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
-  hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(n)), dim3(64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(n)),
+                     dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ constexpr int kBlockSize = 16;         // token slots per KV block
 constexpr int kMaxPartitionTokens = 2048;
 constexpr int kMaxPartitionBlocks = kMaxPartitionTokens / kBlockSize;
 constexpr int kDecodeThreads = 256;    // four 64-lane wavefronts per attention workgroup
+constexpr int kReduceThreads = 256;    // threads of a partition-merge workgroup
 
 struct CacheWriteArgs {
   uint8_t* k_pool;
