@@ -139,6 +139,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     kv_bytes = batch.kv_bytes()
     n_pairs = batch.copy_pairs.shape[0]
+    # tables that share physical blocks (shared prompts) are read through the caches
+    shared = batch.shares_blocks
 
     def step(k, ev=None):
         v = sets[k % len(sets)]
@@ -150,11 +152,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         pa.pa_decode_attention(outs[k % len(sets)], v["query"], v["k_pool"], v["v_pool"], bt, ctx,
-                               cfg.scale, batch.max_context_len, part, ws)
+                               cfg.scale, batch.max_context_len, part, ws, shared_blocks=shared)
         if ev is not None:
             ev[2].record(stream)
         pa.pa_decode_reduce(outs[k % len(sets)], v["query"], v["k_pool"], v["v_pool"], bt, ctx,
-                            cfg.scale, batch.max_context_len, part, ws)
+                            cfg.scale, batch.max_context_len, part, ws, shared_blocks=shared)
         if ev is not None:
             ev[3].record(stream)
 
@@ -226,7 +228,7 @@ def main():
                    "context_lens": list(cfg.ctx), "num_blocks": batch.num_blocks,
                    "partition_size": part, "max_context_len": batch.max_context_len,
                    "kv_bytes_per_step": kv_bytes, "accumulate": "f32",
-                   "copy_pairs": int(n_pairs)},
+                   "copy_pairs": int(n_pairs), "shared_blocks": bool(shared)},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
         "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -67,6 +67,17 @@ typedef enum {
   PA_ERR_LAUNCH = 6,      /* the HIP runtime reported an error when launching */
 } pa_status;
 
+/*
+ * pa_cache_desc.flags bits.
+ *
+ * PA_CACHE_SHARED_BLOCKS: some physical blocks are referenced by several sequences of one
+ *   pa_decode call (shared prompt prefixes, parallel samples; [anal] §4, [dev] copy-on-write).
+ *   pa_decode then reads key/value tiles through the caches so that the sharers reuse them.
+ *   Without it every tile is read as a stream (non-temporal loads that do not allocate in the
+ *   caches), which is faster when each tile is read once. Results are identical either way.
+ */
+#define PA_CACHE_SHARED_BLOCKS 1u
+
 /* Shape of both pools. */
 typedef struct {
   int32_t dtype;        /* pa_dtype of every element in both pools */
@@ -74,6 +85,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* d */
   int32_t block_size;   /* B: token slots per block */
+  uint32_t flags;       /* PA_CACHE_* bits; any other bit gives PA_ERR_UNSUPPORTED */
 } pa_cache_desc;
 
 /*

@@ -21,10 +21,11 @@ import os
 __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
     "pa_decode_reduce", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
-    "pa_abi_version", "ABI_VERSION", "DTYPE_CODES", "EXPORTED_SYMBOLS",
+    "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
+CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpa.so")
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_dec
 class CacheDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("block_size", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class PaError(RuntimeError):
@@ -121,11 +122,11 @@ def _stream(t, stream):
     return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _desc(key_cache, head_dim, block_size) -> CacheDesc:
+def _desc(key_cache, head_dim, block_size, shared_blocks=False) -> CacheDesc:
     if key_cache.dim() != 3 or key_cache.shape[2] != block_size * head_dim:
         raise ValueError("pools must be [num_blocks, num_kv_heads, block_size * head_dim]")
     return CacheDesc(DTYPE_CODES[_dtype_name(key_cache)], key_cache.shape[0], key_cache.shape[1],
-                     head_dim, block_size)
+                     head_dim, block_size, CACHE_SHARED_BLOCKS if shared_blocks else 0)
 
 
 def _check(status: int, where: str) -> None:
@@ -169,10 +170,10 @@ def pa_decode_workspace_bytes(key_cache, num_seqs: int, num_q_heads: int, head_d
 
 
 def _decode_call(fn_name, out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, workspace, block_size, stream):
+                 max_context_len, partition_size, workspace, block_size, shared_blocks, stream):
     import torch
     S, Hq, head_dim = query.shape
-    d = _desc(key_cache, head_dim, block_size)
+    d = _desc(key_cache, head_dim, block_size, shared_blocks)
     if out.shape != query.shape or out.dtype != query.dtype:
         raise ValueError("out must match query in shape and dtype")
     if value_cache.shape != key_cache.shape:
@@ -197,32 +198,34 @@ def _decode_call(fn_name, out, query, key_cache, value_cache, block_tables, cont
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
               max_context_len, partition_size: int = 0, workspace=None, *, block_size: int = 16,
-              stream=None):
+              shared_blocks: bool = False, stream=None):
     """out[s, h] = attention of query[s, h] over sequence s's paged cache (both stages).
 
+    shared_blocks: some physical blocks are referenced by several sequences in this call, so the
+    key/value tiles are read through the caches instead of as a stream (same results).
     Returns the workspace used (allocated with torch when none is given and one is needed).
     """
     return _decode_call("pa_decode", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
-                        block_size, stream)
+                        block_size, shared_blocks, stream)
 
 
 def pa_decode_attention(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size: int = 0, workspace=None, *,
-                        block_size: int = 16, stream=None):
+                        block_size: int = 16, shared_blocks: bool = False, stream=None):
     """First stage of pa_decode only (per-partition attention)."""
     return _decode_call("pa_decode_attention", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
-                        block_size, stream)
+                        block_size, shared_blocks, stream)
 
 
 def pa_decode_reduce(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                      max_context_len, partition_size: int = 0, workspace=None, *,
-                     block_size: int = 16, stream=None):
+                     block_size: int = 16, shared_blocks: bool = False, stream=None):
     """Second stage of pa_decode only (merge of partition states)."""
     return _decode_call("pa_decode_reduce", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
-                        block_size, stream)
+                        block_size, shared_blocks, stream)
 
 
 def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int = 16,

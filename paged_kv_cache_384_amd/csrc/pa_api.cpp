@@ -22,6 +22,7 @@ pa_status check_desc(const pa_cache_desc* c) {
   if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (c->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if ((c->flags & ~PA_CACHE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
   return PA_OK;
 }
@@ -122,6 +123,7 @@ pa_status decode_impl(int stages, const pa_cache_desc* c, const void* key_cache,
   a.num_parts = plan.num_parts;
   a.max_ctx = max_context_len;
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a.stream_kv = (c->flags & PA_CACHE_SHARED_BLOCKS) == 0;
 
   const DType dt = static_cast<DType>(c->dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,8 +50,7 @@ struct RowWeights {
     if constexpr (kPiecesPerRow == 16 && kLoads == 4) {
       // value rows 4*(l/16) + I are scored in lanes 16*(l/16) + 4*I: lane 4*I of the lane's own
       // row of 16, which DPP row_newbcast broadcasts within each row
-      ((w[I] = bits_f32(__builtin_amdgcn_update_dpp(0u, f32_bits(p), 0x150 + 4 * I, 0xF, 0xF,
-                                                    false))), ...);
+      ((w[I] = row_bcast<4 * I>(p)), ...);
     } else {
       const int src = ((lane / kPiecesPerRow) * kLoads) * 16;  // byte address of lane 4*vrow0
       ((w[I] = bits_f32(__builtin_amdgcn_ds_bpermute(src + 16 * I, static_cast<int>(f32_bits(p))))),
@@ -64,7 +63,7 @@ struct RowWeights {
 // kPrefetch: the block is full and the next one (at byte offset offn) is loaded into the key
 // and value registers as soon as each is consumed. Otherwise the block may be the partition's
 // last, so slots at or past len are masked, and nothing is loaded.
-template <DType dt, int D, int NH, bool kPrefetch>
+template <DType dt, int D, int NH, bool kStream, bool kPrefetch>
 struct BlockStep {
   using G = TileGeom<dt, D>;
   static constexpr int kLoads = G::kLoads;
@@ -92,7 +91,7 @@ struct BlockStep {
     }
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) kb[c] = load16(kbase + offn + c * 1024);
+      for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + offn + c * 1024);
     } else {
       const bool valid = j * kBlockSize + (lane >> 2) < len;
 #pragma unroll
@@ -133,12 +132,113 @@ struct BlockStep {
     }
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) vb[i] = load16(vbase + offn + i * G::kRowBytes);
+      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + offn + i * G::kRowBytes);
     }
   }
 };
 
+// Query heads of one workgroup whose scores go to the matrix cores: 16-bit tiles with
+// head_dim 128 and a head group of at least this many query heads.
+constexpr int kMfmaMinHeads = 2;
+
 template <DType dt, int D, int NH>
+constexpr bool use_mfma_scores() {
+  return Elem<dt>::kSize == 2 && D == 128 && NH >= kMfmaMinHeads && NH <= 16;
+}
+
+// The same block step with the scores formed on the matrix cores (16-bit, head_dim 128):
+// S^T (16 tokens x 16 heads) = K (16 tokens x 128 dims) * Q^T (128 dims x 16 heads, heads >= NH
+// zero) as four 16x16x32 MFMAs, one per 1 KiB key chunk row. Lane l loads token l%16, dims
+// [32c + 8(l/16), +8) of chunk row c (a permutation of the row: still one coalesced 1 KiB wave
+// load) and holds head l%16's query slice for the same dims. It receives head l%16's scores of
+// tokens 4(l/16) .. 4(l/16)+3, which are the value rows its own row of 16 lanes accumulates, so
+// lane 16r + h hands head h's weights to its row with DPP row broadcasts. The running maximum m
+// and sum lsum are per lane, for head l%16 (equal in the four rows once reduced).
+template <DType dt, int NH, bool kStream, bool kPrefetch>
+struct MfmaBlockStep {
+  using G = TileGeom<dt, 128>;
+  static constexpr int kLoads = G::kLoads;
+  static constexpr int kEpp = G::kEpp;
+  static_assert(kLoads == 4 && G::kPiecesPerRow == 16, "256-byte rows at block size 16");
+
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  int64_t tile_stride;
+  float scale_log2;
+  int lane;
+  int vrow0;
+  int len;
+
+  template <int... H>
+  __device__ static __forceinline__ void bcast_heads(float x, float (&out)[NH],
+                                                     std::integer_sequence<int, H...>) {
+    ((out[H] = row_bcast<H>(x)), ...);
+  }
+
+  __device__ __forceinline__ void run(int j, int64_t offn, const u32x4 (&qm)[kLoads],
+                                      u32x4 (&kb)[kLoads], u32x4 (&vb)[kLoads], float& m,
+                                      float& lsum, float (&acc)[NH][kEpp]) const {
+    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < kLoads; ++c) d = Mfma16x16x32<dt>::run(kb[c], qm[c], d);
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + offn + c * 1024);
+    }
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = d[i] * scale_log2;
+    if constexpr (!kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = j * kBlockSize + vrow0 + i < len ? sc[i] : -INFINITY;
+    }
+
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleSlack) != 0) {
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float mn = fmaxf(m, bm);
+      const float c = exp2_fast(m - mn);
+      lsum *= c;
+      m = mn;
+      float ch[NH];
+      bcast_heads(c, ch, std::make_integer_sequence<int, NH>{});
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int e = 0; e < kEpp; ++e) acc[hh][e] *= ch[hh];
+    }
+    float pw[4][NH];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pi = exp2_fast(sc[i] - m);
+      lsum += pi;
+      bcast_heads(pi, pw[i], std::make_integer_sequence<int, NH>{});
+    }
+
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      float v[kEpp];
+      Widen<dt>::run(vb[i], v);
+      if constexpr (!kPrefetch) {
+        if (j * kBlockSize + vrow0 + i >= len) {
+#pragma unroll
+          for (int e = 0; e < kEpp; ++e) v[e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(pw[i][hh], v[e], acc[hh][e]);
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + offn + i * G::kRowBytes);
+    }
+  }
+};
+
+template <DType dt, int D, int NH, bool kStream>
 __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
   using G = TileGeom<dt, D>;
   constexpr int kLoads = G::kLoads;
@@ -191,34 +291,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
       bt_s[j] = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
     }
   }
-  // lane l scores token l/4 of each block; it needs query elements
-  // [c*ChunkElems + (l%4)*Epp, +Epp) for each key chunk row c
-  u32x4 qv[NH][kLoads];
-#pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    const uint8_t* qrow =
-        a.query + (static_cast<int64_t>(s) * a.num_q_heads + h0 + hh) * G::kRowBytes;
-#pragma unroll
-    for (int c = 0; c < kLoads; ++c) qv[hh][c] = load16(qrow + c * 64 + (lane & 3) * 16);
-  }
   __syncthreads();
 
+  constexpr bool kMfma = use_mfma_scores<dt, D, NH>();
   const int64_t tile_stride = static_cast<int64_t>(a.num_kv_heads) * G::kTileBytes;
-  const uint8_t* kbase = a.k_pool + static_cast<int64_t>(kvh) * G::kTileBytes + lane * 16;
+  const uint8_t* qbase = a.query + (static_cast<int64_t>(s) * a.num_q_heads + h0) * G::kRowBytes;
+  // key piece c of a lane: VALU scores read byte 16*l of chunk row c (token l/4); matrix-core
+  // scores read byte 64*(l%16) + 16*(l/16) (token l%16)
+  const uint8_t* kbase = a.k_pool + static_cast<int64_t>(kvh) * G::kTileBytes +
+                         (kMfma ? 64 * (lane & 15) + 16 * (lane >> 4) : 16 * lane);
   // value piece i of a lane: row vrow0 + i, bytes [(lane % kPiecesPerRow) * 16, +16)
   const int vrow0 = (lane / kPiecesPerRow) * kLoads;
   const uint8_t* vbase = a.v_pool + static_cast<int64_t>(kvh) * G::kTileBytes +
                          vrow0 * G::kRowBytes + (lane % kPiecesPerRow) * 16;
   const float scale_log2 = a.scale_log2;
 
-  float m[NH], lsum[NH], acc[NH][kEpp];
+  float acc[NH][kEpp];
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
-    m[hh] = -INFINITY;
-    lsum[hh] = 0.0f;
+  for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
     for (int e = 0; e < kEpp; ++e) acc[hh][e] = 0.0f;
-  }
 
   // first block of this wavefront; a wavefront with no block (partitions of fewer than four
   // blocks) loads the partition's last block and never uses it, so that the loads are issued on
@@ -229,44 +321,83 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
     const int64_t off =
         __builtin_amdgcn_readfirstlane(bt_s[j < nblk ? j : nblk - 1]) * tile_stride;
 #pragma unroll
-    for (int c = 0; c < kLoads; ++c) kb[c] = load16(kbase + off + c * 1024);
+    for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + off + c * 1024);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) vb[i] = load16(vbase + off + i * G::kRowBytes);
+    for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + off + i * G::kRowBytes);
   }
   // every block but the wavefront's last: full blocks, next block's loads always issued (so
   // the wait counts stay exact); the wavefront's last block may be the partition's partial
   // one and issues nothing
-  BlockStep<dt, D, NH, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-  for (; j + kWaves < nblk; j += kWaves)
-    full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qv, kb, vb, m,
-             lsum, acc);
-  if (j < nblk) {
-    BlockStep<dt, D, NH, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-    tail.run(j, 0, qv, kb, vb, m, lsum, acc);
+  if constexpr (kMfma) {
+    // query slice of head l%16 (zero for l%16 >= NH), dims [32c + 8(l/16), +8) per chunk row c
+    u32x4 qm[kLoads];
+    const int qh = lane & 15;
+#pragma unroll
+    for (int c = 0; c < kLoads; ++c)
+      qm[c] = qh < NH ? load16(qbase + qh * G::kRowBytes + c * 64 + 16 * (lane >> 4))
+                      : u32x4{0u, 0u, 0u, 0u};
+    float m = -INFINITY, lsum = 0.0f;
+    MfmaBlockStep<dt, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+    for (; j + kWaves < nblk; j += kWaves)
+      full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qm, kb, vb, m,
+               lsum, acc);
+    if (j < nblk) {
+      MfmaBlockStep<dt, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+      tail.run(j, 0, qm, kb, vb, m, lsum, acc);
+    }
+    // lane h (< NH) of any row holds head h's maximum; its sum is spread over the four rows
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (lane < NH) {
+      m_s[wave][lane] = m;
+      l_s[wave][lane] = lsum;
+    }
+  } else {
+    // lane l scores token l/4 of each block; it needs query elements
+    // [c*ChunkElems + (l%4)*Epp, +Epp) of every head for each key chunk row c
+    u32x4 qv[NH][kLoads];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c)
+        qv[hh][c] = load16(qbase + hh * G::kRowBytes + c * 64 + (lane & 3) * 16);
+    float m[NH], lsum[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      m[hh] = -INFINITY;
+      lsum[hh] = 0.0f;
+    }
+    BlockStep<dt, D, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+    for (; j + kWaves < nblk; j += kWaves)
+      full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qv, kb, vb, m,
+               lsum, acc);
+    if (j < nblk) {
+      BlockStep<dt, D, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
+      tail.run(j, 0, qv, kb, vb, m, lsum, acc);
+    }
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      // every token's weight was added in its four scoring lanes
+      lsum[hh] = wave_sum(lsum[hh]) * 0.25f;
+      if (lane == 0) {
+        m_s[wave][hh] = m[hh];
+        l_s[wave][hh] = lsum[hh];
+      }
+    }
   }
 
   // ---- combine lanes holding the same columns, then the four wavefronts -------------------
 #pragma unroll
-  for (int hh = 0; hh < NH; ++hh) {
+  for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
     for (int e = 0; e < kEpp; ++e)
 #pragma unroll
       for (int o = kPiecesPerRow; o < 64; o <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
-    // every token's weight was added in its four scoring lanes
-    lsum[hh] = wave_sum(lsum[hh]) * 0.25f;
-  }
   if (lane < kPiecesPerRow) {
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
       for (int e = 0; e < kEpp; ++e) red_s[wave][hh][lane * kEpp + e] = acc[hh][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      m_s[wave][hh] = m[hh];
-      l_s[wave][hh] = lsum[hh];
-    }
   }
   __syncthreads();
 
@@ -361,8 +492,12 @@ template <DType dt, int D, int NH>
 static hipError_t launch_attn(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n =
       static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.head_groups * a.num_parts;
-  hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH>), dim3(static_cast<unsigned>(n)),
-                     dim3(kDecodeThreads), 0, stream, a);
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true>), dim3(static_cast<unsigned>(n)),
+                       dim3(kDecodeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, false>),
+                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,9 @@ namespace pa {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <DType dt> struct Elem;
 template <> struct Elem<DType::F32> { static constexpr int kSize = 4; };
@@ -35,6 +38,16 @@ struct TileGeom {
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16-byte load of a key or value tile piece. kStream: the tile is read once per launch, so the
+// load carries the non-temporal hint; it does not allocate in L2 or the Infinity Cache, which
+// measurably raises random-tile read bandwidth on MI355X. Otherwise an ordinary cached load, for
+// tiles that several sequences read in the same launch.
+template <bool kStream>
+__device__ __forceinline__ u32x4 load16_kv(const uint8_t* p) {
+  if constexpr (kStream) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
 }
 
 __device__ __forceinline__ void store16(uint8_t* p, u32x4 v) {
@@ -108,6 +121,31 @@ template <> struct Dot16<DType::BF16> {
     return acc;
   }
 };
+
+// c + a * b on the matrix cores: a 16x16 fp32 tile, 32 deep, 16-bit operands. Each operand is
+// one 16-byte piece per lane: A[i][k] in lane i + 16*(k/8), element k%8; B[k][j] in lane
+// j + 16*(k/8), element k%8; the result C[i][j] in lane j + 16*(i/4), element i%4.
+template <DType dt> struct Mfma16x16x32;
+template <> struct Mfma16x16x32<DType::F16> {
+  __device__ static __forceinline__ f32x4 run(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16x16x32<DType::BF16> {
+  __device__ static __forceinline__ f32x4 run(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+// The value of lane L of the caller's own row of 16 lanes, in every lane of that row
+// (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(L >= 0 && L < 16, "lane within a row of 16");
+  return bits_f32(__builtin_amdgcn_update_dpp(0u, f32_bits(x), 0x150 + L, 0xF, 0xF, false));
+}
 
 // Sum over each group of four consecutive lanes, result in all four (two DPP quad swaps).
 __device__ __forceinline__ float quad_sum(float x) {

@@ -61,6 +61,7 @@ struct DecodeArgs {
   int32_t num_parts;    // partitions of the longest context
   int32_t max_ctx;
   float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
+  bool stream_kv;       // read key/value tiles with non-temporal (streaming) loads
 };
 
 // Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).

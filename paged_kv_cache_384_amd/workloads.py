@@ -260,6 +260,11 @@ class DecodeBatch:
     def max_blocks_per_seq(self) -> int:
         return int(self.block_tables.shape[1])
 
+    @property
+    def shares_blocks(self) -> bool:
+        """Whether some physical block is referenced by more than one sequence's table."""
+        return bool((self.ref_counts > 1).any())
+
     def kv_bytes(self) -> int:
         """K plus V bytes the attention must read: every context token, every KV head."""
         c = self.cfg

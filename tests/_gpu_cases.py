@@ -59,11 +59,13 @@ def same_bits(a: np.ndarray, b: np.ndarray, dtype: str) -> bool:
 
 
 def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=True,
-             check_pools=True, value_seed=0):
+             check_pools=True, value_seed=0, shared_blocks=None):
     """Run one step on the GPU and check it against the oracle.
 
     sample: None = every (seq, head) through the oracle; else a list of sequence ids whose
     outputs (all heads) the oracle computes.
+    shared_blocks: the read-policy flag passed to pa_decode (None = whether the batch's tables
+    share blocks).
     Returns a dict of measured errors.
     """
     dev = torch.device("cuda:0")
@@ -113,8 +115,10 @@ def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=
         assert same_bits(to_storage(vp_d), vp, dt), "reshape_and_cache: value pool differs"
     # 3. attention
     out_d = torch.full_like(q_d, float("nan"))
+    if shared_blocks is None:
+        shared_blocks = batch.shares_blocks
     pa.pa_decode(out_d, q_d, kp_d, vp_d, bt_d, ctx_d, cfg.scale, batch.max_context_len,
-                 partition_size)
+                 partition_size, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     out = to_storage(out_d)
     seqs = list(range(cfg.num_seqs)) if sample is None else list(sample)

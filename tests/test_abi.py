@@ -39,8 +39,8 @@ def L():
     return pa.lib()
 
 
-def desc(dtype=1, nb=64, hkv=4, d=128, b=16):
-    return pa.CacheDesc(dtype, nb, hkv, d, b)
+def desc(dtype=1, nb=64, hkv=4, d=128, b=16, flags=0):
+    return pa.CacheDesc(dtype, nb, hkv, d, b, flags)
 
 
 P = ctypes.c_void_p
@@ -77,6 +77,8 @@ def test_decode_validation(L):
     assert decode(L, desc(dtype=7)) == UNSUP
     assert decode(L, desc(d=96)) == UNSUP
     assert decode(L, desc(b=8)) == UNSUP
+    assert decode(L, desc(flags=2)) == UNSUP              # unknown flag bit
+    assert decode(L, desc(flags=0x80000000)) == UNSUP
     assert decode(L, desc(nb=0)) == SHAPE
     assert decode(L, desc(hkv=0)) == SHAPE
     assert decode(L, Hq=6) == SHAPE                      # 6 % 4 != 0
@@ -128,6 +130,7 @@ def test_cache_write_validation(L):
                                       p.get("seq", GOOD), p.get("pos", GOOD), T, P(0))
     assert rc(False) == NULL
     assert rc(desc(dtype=5)) == UNSUP
+    assert rc(desc(flags=4)) == UNSUP
     assert rc(T=-1) == SHAPE
     assert rc(S=0) == SHAPE
     assert rc(maxb=0) == SHAPE

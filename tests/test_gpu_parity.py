@@ -29,9 +29,11 @@ SMALL = [
 def test_small_configs(name, over, parts):
     cfg = wl.config(name, **over)
     for part in parts:
-        log(f"[parity] {name} {over} partition={part}")
-        r = run_step(cfg, partition_size=part)
-        log(f"    max_abs_err={r['max_abs_err']:.3g}")
+        # both read policies (streaming and cached key/value loads) give the same results
+        for shared in (False, True):
+            log(f"[parity] {name} {over} partition={part} shared_blocks={shared}")
+            r = run_step(cfg, partition_size=part, shared_blocks=shared)
+            log(f"    max_abs_err={r['max_abs_err']:.3g}")
 
 
 SHAPES = [(dt, d, hq, hkv) for dt in ("f32", "f16", "bf16") for d in (64, 128)
