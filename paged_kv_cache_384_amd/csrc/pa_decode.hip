@@ -430,7 +430,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   }
 }
 
-// One 256-thread workgroup per (sequence, query head) merges that pair's partition states:
+// The merge for long splits: one 256-thread workgroup per (sequence, query head) merges that
+// pair's partition states:
 // thread t owns column t % D of partition group t / D (partitions p = group, group + G, ...),
 // so every thread streams its partitions' values with independent loads; the G groups are
 // summed through LDS.
@@ -485,6 +486,47 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArg
   }
 }
 
+// The merge for short splits (at most kWaveMergeMaxParts partitions): one wavefront per
+// (sequence, query head), four per workgroup. Lane p holds partition p's max and sum; the
+// weights 2^(m_p - M) are read back one partition at a time as wave-uniform values, and every
+// lane owns D/64 output columns.
+constexpr int kWaveMergeMaxParts = 16;
+
+template <DType dt, int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_wave_kernel(DecodeArgs a) {
+  using G = TileGeom<dt, D>;
+  constexpr int kCols = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 64) + (threadIdx.x >> 6);
+  if (sh >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads) return;
+  const int s = static_cast<int>(sh / a.num_q_heads);
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;  // written directly by the attention kernel
+  const float* m = a.ws_m + sh * a.num_parts;
+  const float* l = a.ws_l + sh * a.num_parts;
+  const float* acc = a.ws_acc + sh * a.num_parts * D + lane * kCols;
+
+  const float mp = lane < np ? m[lane] : -INFINITY;
+  const float M = wave_max(mp);
+  const float w = exp2_fast(mp - M);  // 0 for lanes >= np
+  const float L = wave_sum(lane < np ? w * l[lane] : 0.0f);
+  float o[kCols];
+#pragma unroll
+  for (int e = 0; e < kCols; ++e) o[e] = 0.0f;
+#pragma unroll 4
+  for (int p = 0; p < np; ++p) {
+    const float wp = bits_f32(__builtin_amdgcn_readlane(f32_bits(w), p));
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) o[e] = __builtin_fmaf(wp, acc[p * D + e], o[e]);
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < kCols; ++e)
+    Narrow<dt>::store(a.out + (sh * D + lane * kCols + e) * G::kEsz, o[e] * inv);
+}
+
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
@@ -525,9 +567,16 @@ hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
 
 template <DType dt, int D>
 static hipError_t launch_red(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
-  hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(n)),
-                     dim3(kReduceThreads), 0, stream, a);
+  const int64_t pairs = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  if (a.num_parts <= kWaveMergeMaxParts) {
+    constexpr int kPerWg = kReduceThreads / 64;
+    hipLaunchKernelGGL((decode_reduce_wave_kernel<dt, D>),
+                       dim3(static_cast<unsigned>((pairs + kPerWg - 1) / kPerWg)),
+                       dim3(kReduceThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(pairs)),
+                       dim3(kReduceThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
