@@ -6,11 +6,16 @@ per-partition attention kernel and the partition merge. Inputs are resident in H
 timed region; three independently drawn input sets rotate so that repeated steps are not
 served from the 256 MB Infinity Cache.
 
+Two timed passes of K steps each: an eager pass with HIP events around every kernel (the
+attention kernel's average duration gives ``roofline``), then the timed region proper, where
+the whole step is captured once per input set in a HIP graph and replayed K times (``--eager``
+skips the graph pass and reports the eager step time instead).
+
 Prints one JSON line. ``value`` is KV bytes read per step / step time (GB/s, whole step);
 ``roofline`` reports the attention kernel alone (HIP events on its stream) against the 8 TB/s
 HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--partition P]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--partition P] [--eager]
 """
 from __future__ import annotations
 
@@ -100,6 +105,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager launches only (no HIP-graph replay of the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -164,7 +171,8 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps between two events, synchronised on both sides
+    # pass 1, eager: K whole steps with HIP events on the launch stream around every kernel, for
+    # the per-kernel durations (the attention kernel's average gives the roofline figure)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -176,15 +184,41 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step_eager = t_start.elapsed_time(t_end) / args.steps
     cache_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     attn_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
     red_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
     attn_avg = float(np.mean(attn_us))
-    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us);"
-          f" attention {attn_avg:.1f} us (p10 {np.percentile(attn_us, 10):.1f}, p90 "
-          f"{np.percentile(attn_us, 90):.1f}), reduce {np.mean(red_us):.1f} us, cache write "
-          f"{np.mean(cache_us):.1f} us", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} eager steps: {ms_step_eager * 1e3:.1f} us/step (wall "
+          f"{wall / args.steps * 1e6:.1f} us); attention {attn_avg:.1f} us (p10 "
+          f"{np.percentile(attn_us, 10):.1f}, p90 {np.percentile(attn_us, 90):.1f}), reduce "
+          f"{np.mean(red_us):.1f} us, cache write {np.mean(cache_us):.1f} us",
+          file=sys.stderr, flush=True)
+
+    # pass 2, the timed region: the whole step captured once per input set in a HIP graph (the
+    # library allocates nothing and every launch goes to torch's current stream, which is the
+    # capture stream), then K replays between two events, synchronised on both sides
+    ms_step = ms_step_eager
+    if not args.eager:
+        graphs = []
+        for k in range(len(sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        g_start = torch.cuda.Event(enable_timing=True)
+        g_end = torch.cuda.Event(enable_timing=True)
+        g_start.record()
+        for k in range(args.steps):
+            graphs[k % len(graphs)].replay()
+        g_end.record()
+        torch.cuda.synchronize()
+        ms_step = g_start.elapsed_time(g_end) / args.steps
+        print(f"[bench] {args.steps} graph-replayed steps: {ms_step * 1e3:.1f} us/step",
+              file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         n = 1 << 30
@@ -231,6 +265,8 @@ def main():
                    "copy_pairs": int(n_pairs), "shared_blocks": bool(shared)},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
+        "launch": "eager" if args.eager else "hip_graph",
+        "ms_per_step_eager": round(ms_step_eager, 5),
         "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),
                       "attention": round(attn_avg, 2),
                       "partition_reduce": round(float(np.mean(red_us)), 2)},
