@@ -1,4 +1,4 @@
-// Decode attention over the paged KV cache, and the merge of partition states.
+// Decode attention over the paged KV cache (the partition merge is in pa_reduce.hip).
 //
 // Sources (page title, section):
 //   "PagedAttention" (newikis.com), "수학적 공식": dense causal attention of the newest token
@@ -246,7 +246,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   constexpr int kPiecesPerRow = G::kPiecesPerRow;
   constexpr int kWaves = kDecodeThreads / 64;
 
-  __shared__ int bt_s[kMaxPartitionBlocks];
   __shared__ float red_s[kWaves][NH][D];
   __shared__ float m_s[kWaves][NH];
   __shared__ float l_s[kWaves][NH];
@@ -282,16 +281,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   const int nblk = (len + kBlockSize - 1) / kBlockSize;
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
 
-  // ---- stage the block-table slice and the query pieces -------------------------------------
-  {
-    const int32_t* row =
-        a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
-    for (int j = tid; j < nblk; j += kDecodeThreads) {
-      const int id = row[j];
-      bt_s[j] = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-    }
-  }
-  __syncthreads();
+  // ---- this wavefront's blocks ------------------------------------------------------------
+  // a contiguous range [jb, je) of the partition's blocks; their physical ids are wave-uniform
+  // and come straight from the table with scalar loads, clamped into [0, NB)
+  const int32_t* bt_row =
+      a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
+  const int per_wave = nblk / kWaves;
+  const int extra = nblk % kWaves;
+  const int jb = wave * per_wave + min(wave, extra);
+  const int je = jb + per_wave + (wave < extra ? 1 : 0);
+  const int num_blocks = a.num_blocks;
+  auto block_id = [&](int j) {
+    const int id = bt_row[j];
+    return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+  };
 
   constexpr bool kMfma = use_mfma_scores<dt, D, NH>();
   const int64_t tile_stride = static_cast<int64_t>(a.num_kv_heads) * G::kTileBytes;
@@ -316,10 +319,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   // blocks) loads the partition's last block and never uses it, so that the loads are issued on
   // every path and the compiler's wait counts for the loop stay exact
   u32x4 kb[kLoads], vb[kLoads];
-  int j = wave;
+  int j = jb;
   {
-    const int64_t off =
-        __builtin_amdgcn_readfirstlane(bt_s[j < nblk ? j : nblk - 1]) * tile_stride;
+    const int64_t off = block_id(j < je ? j : nblk - 1) * tile_stride;
 #pragma unroll
     for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + off + c * 1024);
 #pragma unroll
@@ -338,10 +340,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
                       : u32x4{0u, 0u, 0u, 0u};
     float m = -INFINITY, lsum = 0.0f;
     MfmaBlockStep<dt, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-    for (; j + kWaves < nblk; j += kWaves)
-      full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qm, kb, vb, m,
+    for (; j + 1 < je; ++j)
+      full.run(j, block_id(j + 1) * tile_stride, qm, kb, vb, m,
                lsum, acc);
-    if (j < nblk) {
+    if (j < je) {
       MfmaBlockStep<dt, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
       tail.run(j, 0, qm, kb, vb, m, lsum, acc);
     }
@@ -368,10 +370,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
       lsum[hh] = 0.0f;
     }
     BlockStep<dt, D, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-    for (; j + kWaves < nblk; j += kWaves)
-      full.run(j, __builtin_amdgcn_readfirstlane(bt_s[j + kWaves]) * tile_stride, qv, kb, vb, m,
+    for (; j + 1 < je; ++j)
+      full.run(j, block_id(j + 1) * tile_stride, qv, kb, vb, m,
                lsum, acc);
-    if (j < nblk) {
+    if (j < je) {
       BlockStep<dt, D, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
       tail.run(j, 0, qv, kb, vb, m, lsum, acc);
     }
@@ -430,103 +432,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   }
 }
 
-// The merge for long splits: one 256-thread workgroup per (sequence, query head) merges that
-// pair's partition states:
-// thread t owns column t % D of partition group t / D (partitions p = group, group + G, ...),
-// so every thread streams its partitions' values with independent loads; the G groups are
-// summed through LDS.
-template <DType dt, int D>
-__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArgs a) {
-  using G = TileGeom<dt, D>;
-  constexpr int kGroups = kReduceThreads / D;
-  __shared__ float red_s[kReduceThreads];
-  __shared__ float lred_s[kGroups];
-  __shared__ float wmax_s[kReduceThreads / 64];
-
-  const int sh = blockIdx.x;
-  const int s = sh / a.num_q_heads;
-  int ctx = a.context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;  // written directly by the attention kernel
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const float* m = a.ws_m + static_cast<int64_t>(sh) * a.num_parts;
-  const float* l = a.ws_l + static_cast<int64_t>(sh) * a.num_parts;
-  const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
-
-  float M = -INFINITY;
-  for (int p = tid; p < np; p += kReduceThreads) M = fmaxf(M, m[p]);
-  M = wave_max(M);
-  if (lane == 0) wmax_s[tid >> 6] = M;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kReduceThreads / 64; ++w) M = fmaxf(M, wmax_s[w]);
-
-  const int col = tid % D;
-  const int grp = tid / D;
-  float o = 0.0f, L = 0.0f;
-#pragma unroll 8
-  for (int p = grp; p < np; p += kGroups) {
-    const float w = exp2_fast(m[p] - M);
-    o = __builtin_fmaf(w, acc[static_cast<int64_t>(p) * D + col], o);
-    L = __builtin_fmaf(w, l[p], L);
-  }
-  red_s[tid] = o;
-  if (col == 0) lred_s[grp] = L;
-  __syncthreads();
-  if (tid < D) {
-    float ot = 0.0f, lt = 0.0f;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      ot += red_s[g * D + tid];
-      lt += lred_s[g];
-    }
-    Narrow<dt>::store(a.out + (static_cast<int64_t>(sh) * D + tid) * G::kEsz, ot / lt);
-  }
-}
-
-// The merge for short splits (at most kWaveMergeMaxParts partitions): one wavefront per
-// (sequence, query head), four per workgroup. Lane p holds partition p's max and sum; the
-// weights 2^(m_p - M) are read back one partition at a time as wave-uniform values, and every
-// lane owns D/64 output columns.
-constexpr int kWaveMergeMaxParts = 16;
-
-template <DType dt, int D>
-__global__ __launch_bounds__(kReduceThreads) void decode_reduce_wave_kernel(DecodeArgs a) {
-  using G = TileGeom<dt, D>;
-  constexpr int kCols = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t sh = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 64) + (threadIdx.x >> 6);
-  if (sh >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads) return;
-  const int s = static_cast<int>(sh / a.num_q_heads);
-  int ctx = a.context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;  // written directly by the attention kernel
-  const float* m = a.ws_m + sh * a.num_parts;
-  const float* l = a.ws_l + sh * a.num_parts;
-  const float* acc = a.ws_acc + sh * a.num_parts * D + lane * kCols;
-
-  const float mp = lane < np ? m[lane] : -INFINITY;
-  const float M = wave_max(mp);
-  const float w = exp2_fast(mp - M);  // 0 for lanes >= np
-  const float L = wave_sum(lane < np ? w * l[lane] : 0.0f);
-  float o[kCols];
-#pragma unroll
-  for (int e = 0; e < kCols; ++e) o[e] = 0.0f;
-#pragma unroll 4
-  for (int p = 0; p < np; ++p) {
-    const float wp = bits_f32(__builtin_amdgcn_readlane(f32_bits(w), p));
-#pragma unroll
-    for (int e = 0; e < kCols; ++e) o[e] = __builtin_fmaf(wp, acc[p * D + e], o[e]);
-  }
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int e = 0; e < kCols; ++e)
-    Narrow<dt>::store(a.out + (sh * D + lane * kCols + e) * G::kEsz, o[e] * inv);
-}
-
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
@@ -561,34 +466,6 @@ hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
                                            : launch_attn_nh<DType::F16, 128>(a, stream);
     case DType::BF16: return head_dim == 64 ? launch_attn_nh<DType::BF16, 64>(a, stream)
                                             : launch_attn_nh<DType::BF16, 128>(a, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <DType dt, int D>
-static hipError_t launch_red(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t pairs = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
-  if (a.num_parts <= kWaveMergeMaxParts) {
-    constexpr int kPerWg = kReduceThreads / 64;
-    hipLaunchKernelGGL((decode_reduce_wave_kernel<dt, D>),
-                       dim3(static_cast<unsigned>((pairs + kPerWg - 1) / kPerWg)),
-                       dim3(kReduceThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(pairs)),
-                       dim3(kReduceThreads), 0, stream, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_parts <= 1) return hipSuccess;
-  switch (dt) {
-    case DType::F32: return head_dim == 64 ? launch_red<DType::F32, 64>(a, stream)
-                                           : launch_red<DType::F32, 128>(a, stream);
-    case DType::F16: return head_dim == 64 ? launch_red<DType::F16, 64>(a, stream)
-                                           : launch_red<DType::F16, 128>(a, stream);
-    case DType::BF16: return head_dim == 64 ? launch_red<DType::BF16, 64>(a, stream)
-                                            : launch_red<DType::BF16, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }

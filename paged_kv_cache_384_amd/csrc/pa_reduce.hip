@@ -1,0 +1,148 @@
+// Merge of the partition states the attention kernel leaves when a context is split into
+// several partitions (split-K over the context).
+//
+// Source (page title, section): "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리"
+// (ryotta.opik.net), §3: the block-wise kernel only groups the partial sums of ordinary
+// attention differently, so partial softmax states can be combined in any grouping. Each
+// partition p of a (sequence, head) holds its maximum m_p (base-2 domain), its sum
+// l_p = sum 2^(z - m_p) and its unnormalised output acc_p = sum 2^(z - m_p) v; with M = max m_p,
+//     out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+#include "pa_device.h"
+
+namespace pa {
+
+// The merge for long splits: one 256-thread workgroup per (sequence, query head) merges that
+// pair's partition states:
+// thread t owns column t % D of partition group t / D (partitions p = group, group + G, ...),
+// so every thread streams its partitions' values with independent loads; the G groups are
+// summed through LDS.
+template <DType dt, int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArgs a) {
+  using G = TileGeom<dt, D>;
+  constexpr int kGroups = kReduceThreads / D;
+  __shared__ float red_s[kReduceThreads];
+  __shared__ float lred_s[kGroups];
+  __shared__ float wmax_s[kReduceThreads / 64];
+
+  const int sh = blockIdx.x;
+  const int s = sh / a.num_q_heads;
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;  // written directly by the attention kernel
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const float* m = a.ws_m + static_cast<int64_t>(sh) * a.num_parts;
+  const float* l = a.ws_l + static_cast<int64_t>(sh) * a.num_parts;
+  const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
+
+  float M = -INFINITY;
+  for (int p = tid; p < np; p += kReduceThreads) M = fmaxf(M, m[p]);
+  M = wave_max(M);
+  if (lane == 0) wmax_s[tid >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kReduceThreads / 64; ++w) M = fmaxf(M, wmax_s[w]);
+
+  const int col = tid % D;
+  const int grp = tid / D;
+  float o = 0.0f, L = 0.0f;
+#pragma unroll 8
+  for (int p = grp; p < np; p += kGroups) {
+    const float w = exp2_fast(m[p] - M);
+    o = __builtin_fmaf(w, acc[static_cast<int64_t>(p) * D + col], o);
+    L = __builtin_fmaf(w, l[p], L);
+  }
+  red_s[tid] = o;
+  if (col == 0) lred_s[grp] = L;
+  __syncthreads();
+  if (tid < D) {
+    float ot = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      ot += red_s[g * D + tid];
+      lt += lred_s[g];
+    }
+    Narrow<dt>::store(a.out + (static_cast<int64_t>(sh) * D + tid) * G::kEsz, ot / lt);
+  }
+}
+
+// The merge for short splits (at most kWaveMergeMaxParts partitions): one wavefront per
+// (sequence, query head), four per workgroup. Lane p holds partition p's max and sum; every lane
+// owns D/64 output columns, loads them for all partitions at once, and weighs them with
+// 2^(m_p - M) read back from lane p as a wave-uniform value.
+constexpr int kWaveMergeMaxParts = 16;
+
+template <DType dt, int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_wave_kernel(DecodeArgs a) {
+  using G = TileGeom<dt, D>;
+  constexpr int kCols = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * (kReduceThreads / 64) + (threadIdx.x >> 6);
+  if (sh >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads) return;
+  const int s = static_cast<int>(sh / a.num_q_heads);
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;  // written directly by the attention kernel
+  const float* m = a.ws_m + sh * a.num_parts;
+  const float* l = a.ws_l + sh * a.num_parts;
+  const float* acc = a.ws_acc + sh * a.num_parts * D + lane * kCols;
+
+  const float mp = lane < np ? m[lane] : -INFINITY;
+  const float M = wave_max(mp);
+  const float w = exp2_fast(mp - M);  // 0 for lanes >= np
+  const float L = wave_sum(lane < np ? w * l[lane] : 0.0f);
+  // every partition's values are requested before the first is used
+  float r[kWaveMergeMaxParts][kCols];
+#pragma unroll
+  for (int p = 0; p < kWaveMergeMaxParts; ++p)
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) r[p][e] = p < np ? acc[p * D + e] : 0.0f;
+  float o[kCols];
+#pragma unroll
+  for (int e = 0; e < kCols; ++e) o[e] = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kWaveMergeMaxParts; ++p) {
+    const float wp = bits_f32(__builtin_amdgcn_readlane(f32_bits(w), p));  // 0 for p >= np
+#pragma unroll
+    for (int e = 0; e < kCols; ++e) o[e] = __builtin_fmaf(wp, r[p][e], o[e]);
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < kCols; ++e)
+    Narrow<dt>::store(a.out + (sh * D + lane * kCols + e) * G::kEsz, o[e] * inv);
+}
+
+// ------------------------------------------------------------------------------------------
+// launcher
+// ------------------------------------------------------------------------------------------
+template <DType dt, int D>
+static hipError_t launch_red(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t pairs = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  if (a.num_parts <= kWaveMergeMaxParts) {
+    constexpr int kPerWg = kReduceThreads / 64;
+    hipLaunchKernelGGL((decode_reduce_wave_kernel<dt, D>),
+                       dim3(static_cast<unsigned>((pairs + kPerWg - 1) / kPerWg)),
+                       dim3(kReduceThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<dt, D>), dim3(static_cast<unsigned>(pairs)),
+                       dim3(kReduceThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_parts <= 1) return hipSuccess;
+  switch (dt) {
+    case DType::F32: return head_dim == 64 ? launch_red<DType::F32, 64>(a, stream)
+                                           : launch_red<DType::F32, 128>(a, stream);
+    case DType::F16: return head_dim == 64 ? launch_red<DType::F16, 64>(a, stream)
+                                           : launch_red<DType::F16, 128>(a, stream);
+    case DType::BF16: return head_dim == 64 ? launch_red<DType::BF16, 64>(a, stream)
+                                            : launch_red<DType::BF16, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
