@@ -60,9 +60,9 @@ struct RowWeights {
 };
 
 // One block of one wavefront's stream: scores, running-softmax update, weighted values.
-// kPrefetch: the block is full and the next one (at byte offset offn) is loaded into the key
-// and value registers as soon as each is consumed. Otherwise the block may be the partition's
-// last, so slots at or past len are masked, and nothing is loaded.
+// kPrefetch: the block is full and its registers are refilled with the block at byte offset
+// offn as soon as the keys and then the values are consumed. Otherwise the block may be the
+// partition's last, so slots at or past len are masked, and nothing is loaded.
 template <DType dt, int D, int NH, bool kStream, bool kPrefetch>
 struct BlockStep {
   using G = TileGeom<dt, D>;
@@ -70,6 +70,7 @@ struct BlockStep {
   static constexpr int kEpp = G::kEpp;
   static constexpr int kPiecesPerRow = G::kPiecesPerRow;
 
+  const u32x4 (&qv)[NH][kLoads];
   const uint8_t* kbase;
   const uint8_t* vbase;
   int64_t tile_stride;
@@ -78,9 +79,9 @@ struct BlockStep {
   int vrow0;
   int len;
 
-  __device__ __forceinline__ void run(int j, int64_t offn, const u32x4 (&qv)[NH][kLoads],
-                                      u32x4 (&kb)[kLoads], u32x4 (&vb)[kLoads], float (&m)[NH],
-                                      float (&lsum)[NH], float (&acc)[NH][kEpp]) const {
+  __device__ __forceinline__ void run(int j, int64_t offn, u32x4 (&kb)[kLoads],
+                                      u32x4 (&vb)[kLoads], float (&m)[NH], float (&lsum)[NH],
+                                      float (&acc)[NH][kEpp]) const {
     float sc[NH];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -161,6 +162,7 @@ struct MfmaBlockStep {
   static constexpr int kEpp = G::kEpp;
   static_assert(kLoads == 4 && G::kPiecesPerRow == 16, "256-byte rows at block size 16");
 
+  const u32x4 (&qm)[kLoads];
   const uint8_t* kbase;
   const uint8_t* vbase;
   int64_t tile_stride;
@@ -175,9 +177,9 @@ struct MfmaBlockStep {
     ((out[H] = row_bcast<H>(x)), ...);
   }
 
-  __device__ __forceinline__ void run(int j, int64_t offn, const u32x4 (&qm)[kLoads],
-                                      u32x4 (&kb)[kLoads], u32x4 (&vb)[kLoads], float& m,
-                                      float& lsum, float (&acc)[NH][kEpp]) const {
+  __device__ __forceinline__ void run(int j, int64_t offn, u32x4 (&kb)[kLoads],
+                                      u32x4 (&vb)[kLoads], float& m, float& lsum,
+                                      float (&acc)[NH][kEpp]) const {
     f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < kLoads; ++c) d = Mfma16x16x32<dt>::run(kb[c], qm[c], d);
@@ -315,38 +317,84 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
 #pragma unroll
     for (int e = 0; e < kEpp; ++e) acc[hh][e] = 0.0f;
 
-  // first block of this wavefront; a wavefront with no block (partitions of fewer than four
-  // blocks) loads the partition's last block and never uses it, so that the loads are issued on
-  // every path and the compiler's wait counts for the loop stay exact
-  u32x4 kb[kLoads], vb[kLoads];
-  int j = jb;
-  {
-    const int64_t off = block_id(j < je ? j : nblk - 1) * tile_stride;
-#pragma unroll
-    for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + off + c * 1024);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + off + i * G::kRowBytes);
-  }
-  // every block but the wavefront's last: full blocks, next block's loads always issued (so
-  // the wait counts stay exact); the wavefront's last block may be the partition's partial
-  // one and issues nothing
+  // the query pieces are requested first: they are older than every block load, so waiting
+  // for them never waits for a block
+  // matrix-core scores: head l%16's slice (zero for l%16 >= NH), dims [32c + 8(l/16), +8) of
+  // chunk row c; VALU scores: lane l scores token l/4 and needs dims [c*ChunkElems +
+  // (l%4)*Epp, +Epp) of every head for each chunk row c
+  [[maybe_unused]] u32x4 qm[kLoads];
+  [[maybe_unused]] u32x4 qv[kMfma ? 1 : NH][kLoads];
   if constexpr (kMfma) {
-    // query slice of head l%16 (zero for l%16 >= NH), dims [32c + 8(l/16), +8) per chunk row c
-    u32x4 qm[kLoads];
     const int qh = lane & 15;
 #pragma unroll
     for (int c = 0; c < kLoads; ++c)
       qm[c] = qh < NH ? load16(qbase + qh * G::kRowBytes + c * 64 + 16 * (lane >> 4))
                       : u32x4{0u, 0u, 0u, 0u};
-    float m = -INFINITY, lsum = 0.0f;
-    MfmaBlockStep<dt, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-    for (; j + 1 < je; ++j)
-      full.run(j, block_id(j + 1) * tile_stride, qm, kb, vb, m,
-               lsum, acc);
-    if (j < je) {
-      MfmaBlockStep<dt, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-      tail.run(j, 0, qm, kb, vb, m, lsum, acc);
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c)
+        qv[hh][c] = load16(qbase + hh * G::kRowBytes + c * 64 + (lane & 3) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the scheduler from moving block loads above these
+
+  // Key/value loads in flight per wavefront: kDepth blocks ahead of the one being computed.
+  // One register set (kA, vA) per block in flight; a step consumes its set and refills it with
+  // the block kDepth ahead. Inside the loops every load is issued unconditionally (a wavefront
+  // with fewer than kDepth blocks loads the partition's last block in their place and never
+  // uses it), so the compiler's wait counts stay exact; only the wavefront's last kDepth
+  // blocks, which may include the partition's partial one, run without refilling. Two blocks
+  // ahead pays off for streamed single-head workgroups with 4 KiB tiles; with more heads, 8 KiB
+  // tiles or cached reads of shared blocks the extra registers cost more occupancy than the
+  // deeper pipeline gains (measured on MI355X).
+  constexpr int kDepth = NH == 1 && kLoads <= 4 && kStream ? 2 : 1;
+  u32x4 kA[kLoads], vA[kLoads];
+  [[maybe_unused]] u32x4 kB[kLoads], vB[kLoads];
+  auto load_block = [&](int jj, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads]) {
+    const int64_t off = block_id(jj < je ? jj : nblk - 1) * tile_stride;
+#pragma unroll
+    for (int c = 0; c < kLoads; ++c) kr[c] = load16_kv<kStream>(kbase + off + c * 1024);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) vr[i] = load16_kv<kStream>(vbase + off + i * G::kRowBytes);
+  };
+  load_block(jb, kA, vA);
+  if constexpr (kDepth == 2) load_block(jb + 1, kB, vB);
+
+  // drives one step type over the wavefront's blocks [jb, je)
+  auto stream_blocks = [&](auto& full, auto& tail, auto&... state) {
+    int j = jb;
+    if constexpr (kDepth == 1) {
+      for (; j + 1 < je; ++j) full.run(j, block_id(j + 1) * tile_stride, kA, vA, state...);
+      if (j < je) tail.run(j, 0, kA, vA, state...);
+    } else {
+      // pairs of full steps while at least four blocks remain (kA holds block j, kB block
+      // j + 1 at the top of each pair), then the last one to three blocks
+      for (; j + 3 < je; j += 2) {
+        full.run(j, block_id(j + 2) * tile_stride, kA, vA, state...);
+        full.run(j + 1, block_id(j + 3) * tile_stride, kB, vB, state...);
+      }
+      const int left = je - j;
+      if (left == 3) {
+        full.run(j, block_id(j + 2) * tile_stride, kA, vA, state...);
+        tail.run(j + 1, 0, kB, vB, state...);
+        tail.run(j + 2, 0, kA, vA, state...);
+      } else if (left == 2) {
+        tail.run(j, 0, kA, vA, state...);
+        tail.run(j + 1, 0, kB, vB, state...);
+      } else if (left == 1) {
+        tail.run(j, 0, kA, vA, state...);
+      }
     }
+  };
+
+  if constexpr (kMfma) {
+    float m = -INFINITY, lsum = 0.0f;
+    MfmaBlockStep<dt, NH, kStream, true> full{qm, kbase, vbase, tile_stride, scale_log2, lane,
+                                              vrow0, len};
+    MfmaBlockStep<dt, NH, kStream, false> tail{qm, kbase, vbase, tile_stride, scale_log2, lane,
+                                               vrow0, len};
+    stream_blocks(full, tail, m, lsum, acc);
     // lane h (< NH) of any row holds head h's maximum; its sum is spread over the four rows
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -355,28 +403,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
       l_s[wave][lane] = lsum;
     }
   } else {
-    // lane l scores token l/4 of each block; it needs query elements
-    // [c*ChunkElems + (l%4)*Epp, +Epp) of every head for each key chunk row c
-    u32x4 qv[NH][kLoads];
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-      for (int c = 0; c < kLoads; ++c)
-        qv[hh][c] = load16(qbase + hh * G::kRowBytes + c * 64 + (lane & 3) * 16);
     float m[NH], lsum[NH];
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       m[hh] = -INFINITY;
       lsum[hh] = 0.0f;
     }
-    BlockStep<dt, D, NH, kStream, true> full{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-    for (; j + 1 < je; ++j)
-      full.run(j, block_id(j + 1) * tile_stride, qv, kb, vb, m,
-               lsum, acc);
-    if (j < je) {
-      BlockStep<dt, D, NH, kStream, false> tail{kbase, vbase, tile_stride, scale_log2, lane, vrow0, len};
-      tail.run(j, 0, qv, kb, vb, m, lsum, acc);
-    }
+    BlockStep<dt, D, NH, kStream, true> full{qv, kbase, vbase, tile_stride, scale_log2, lane,
+                                             vrow0, len};
+    BlockStep<dt, D, NH, kStream, false> tail{qv, kbase, vbase, tile_stride, scale_log2, lane,
+                                              vrow0, len};
+    stream_blocks(full, tail, m, lsum, acc);
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       // every token's weight was added in its four scoring lanes
