@@ -94,6 +94,66 @@ def cpu_baseline(batch, host, budget_s: float):
             "seconds": round(dt, 2), "tokens_per_s": round(done / dt, 3)}
 
 
+def paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream):
+    """Whole pa_decode calls (attention + merge), HIP events on the launch stream, K calls each:
+    paged over the batch as drawn (shuffled placement), paged over a contiguously laid out copy
+    (identity tables), and the contiguous twin over that copy (no table at all)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_384_amd as pa
+    from paged_kv_cache_384_amd import workloads as wl
+    if shared:
+        return {"skipped": "sequences share blocks; a contiguous layout cannot hold the batch"}
+    dev = sets[0]["query"].device
+    cb = wl.build_batch(wl.config(cfg.name, placement="contiguous"))
+    csets = [wl.make_values(cb, device=dev, seed=10 + k, poison_nan=False)
+             for k in range(len(sets))]
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    cbt = torch.from_numpy(cb.block_tables).to(dev)
+    ctx = torch.from_numpy(batch.context_lens).to(dev)
+    W = cb.max_blocks_per_seq
+    mx = batch.max_context_len
+
+    def paged(k):
+        v = sets[k % len(sets)]
+        pa.pa_decode(outs[k % len(outs)], v["query"], v["k_pool"], v["v_pool"], bt, ctx,
+                     cfg.scale, mx, part, ws)
+
+    def paged_identity(k):
+        v = csets[k % len(csets)]
+        pa.pa_decode(outs[k % len(outs)], v["query"], v["k_pool"], v["v_pool"], cbt, ctx,
+                     cfg.scale, mx, part, ws)
+
+    def twin(k):
+        v = csets[k % len(csets)]
+        pa.pa_decode_contiguous(outs[k % len(outs)], v["query"], v["k_pool"], v["v_pool"], ctx,
+                                cfg.scale, mx, W, part, ws)
+
+    res = {}
+    for name, fn in (("paged_shuffled_us", paged), ("paged_identity_us", paged_identity),
+                     ("contiguous_us", twin)):
+        for k in range(args.warmup):
+            fn(k)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            evs[k][0].record(stream)
+            fn(k)
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs])), 2)
+    c = res["contiguous_us"]
+    res["slowdown_shuffled"] = round(res["paged_shuffled_us"] / c - 1.0, 4)
+    res["slowdown_identity"] = round(res["paged_identity_us"] / c - 1.0, 4)
+    print(f"[bench] paging overhead: paged (shuffled) {res['paged_shuffled_us']} us, paged "
+          f"(identity tables) {res['paged_identity_us']} us, contiguous twin {c} us",
+          file=sys.stderr, flush=True)
+    del csets
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +167,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time the eager launches only (no HIP-graph replay of the step)")
+    ap.add_argument("--paging-overhead", action="store_true",
+                    help="also time pa_decode against its contiguous twin (no block table) on a "
+                         "contiguously laid out copy of the batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -237,6 +300,10 @@ def main():
                 "kernel": "decode_attention_kernel", "avg_us": round(attn_avg, 2),
                 "bytes_per_launch": kv_bytes}
 
+    paging = None
+    if args.paging_overhead:
+        paging = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         host = {name: host_storage(sets[0][name]) for name in ("query", "k_pool", "v_pool")}
@@ -273,6 +340,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if paging is not None:
+        line["paging_overhead"] = paging
     print(json.dumps(line), flush=True)
 
 

@@ -182,6 +182,25 @@ pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_contiguous — the same decode attention over a KV cache that is not paged: the
+ * contiguous twin, kept to measure what paging costs. ([anal] §3 compares the paged kernel with
+ * an ordinary one over contiguous keys and values and puts it about 20-26% slower.)
+ *
+ * There is no block table: logical block j of sequence s is physical block
+ * s * max_blocks_per_seq + j of the pools (same layout, same partitions and merge as pa_decode),
+ * so the result equals pa_decode's with block_tables[s][j] = s * max_blocks_per_seq + j.
+ * Arguments as pa_decode without block_tables. Contiguous sequences never share blocks, so the
+ * key/value tiles are always streamed; PA_CACHE_SHARED_BLOCKS gives PA_ERR_UNSUPPORTED.
+ * num_seqs * max_blocks_per_seq > num_blocks gives PA_ERR_SHAPE.
+ */
+pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
+                               const void* value_cache, void* out, const void* query,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, float scale,
+                               int32_t max_context_len, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * pa_copy_blocks — duplicate whole physical blocks (copy-on-write).
  * ([anal] §4 and [dev]: a sharer about to write into a block whose reference count exceeds one
  *  gets a fresh block holding a copy of the old contents; [blog] ②.)

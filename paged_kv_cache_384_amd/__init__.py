@@ -20,7 +20,7 @@ import os
 
 __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
-    "pa_decode_reduce", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
+    "pa_decode_reduce", "pa_decode_contiguous", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
@@ -31,8 +31,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
-                    "pa_decode_attention", "pa_decode_reduce", "pa_copy_blocks",
-                    "pa_status_string", "pa_abi_version"]
+                    "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
+                    "pa_copy_blocks", "pa_status_string", "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
             getattr(L, name).argtypes = _DECODE_ARGS
             getattr(L, name).restype = ctypes.c_int
+        L.pa_decode_contiguous.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                           ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t, _vp]
+        L.pa_decode_contiguous.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_desc_p, _vp, _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -226,6 +229,33 @@ def pa_decode_reduce(out, query, key_cache, value_cache, block_tables, context_l
     return _decode_call("pa_decode_reduce", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
                         block_size, shared_blocks, stream)
+
+
+def pa_decode_contiguous(out, query, key_cache, value_cache, context_lens, scale, max_context_len,
+                         max_blocks_per_seq, partition_size: int = 0, workspace=None, *,
+                         block_size: int = 16, stream=None):
+    """The contiguous twin of pa_decode: sequence s's block j is physical block
+    s * max_blocks_per_seq + j (no block table). Returns the workspace used."""
+    import torch
+    S, Hq, head_dim = query.shape
+    d = _desc(key_cache, head_dim, block_size)
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query in shape and dtype")
+    if value_cache.shape != key_cache.shape or context_lens.numel() != S:
+        raise ValueError("pools differ in shape, or context_lens is not [num_seqs]")
+    need = pa_decode_workspace_bytes(key_cache, S, Hq, head_dim, max_context_len, partition_size,
+                                     block_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else _vp(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache", query.dtype),
+            _dev(value_cache, "value_cache", query.dtype), _dev(out, "out"),
+            _dev(query, "query"), int(max_blocks_per_seq),
+            _dev(context_lens, "context_lens", torch.int32), S, Hq, float(scale),
+            int(max_context_len), int(partition_size), ws_ptr, ws_bytes, _stream(query, stream))
+    _check(lib().pa_decode_contiguous(*args), "pa_decode_contiguous")
+    return workspace
 
 
 def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int = 16,

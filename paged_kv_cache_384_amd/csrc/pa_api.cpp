@@ -76,7 +76,9 @@ pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_he
   return PA_OK;
 }
 
-pa_status decode_impl(int stages, const pa_cache_desc* c, const void* key_cache,
+// paged = false: the contiguous twin (no table; sequence s's block j is physical block
+// s * max_blocks_per_seq + j), block_tables unused.
+pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void* key_cache,
                       const void* value_cache, void* out, const void* query,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -88,11 +90,16 @@ pa_status decode_impl(int stages, const pa_cache_desc* c, const void* key_cache,
   if (max_blocks_per_seq <= 0 ||
       static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
     return PA_ERR_SHAPE;
+  if (!paged) {
+    // contiguous sequences cannot share blocks, and every sequence's span must fit the pool
+    if (c->flags & PA_CACHE_SHARED_BLOCKS) return PA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq > c->num_blocks) return PA_ERR_SHAPE;
+  }
   if (num_seqs == 0) return PA_OK;
-  if (!key_cache || !value_cache || !out || !query || !block_tables || !context_lens)
+  if (!key_cache || !value_cache || !out || !query || (paged && !block_tables) || !context_lens)
     return PA_ERR_NULL;
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(out, 16) ||
-      !aligned(query, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      !aligned(query, 16) || (paged && !aligned(block_tables, 4)) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
   if (plan.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return PA_ERR_WORKSPACE;
@@ -124,6 +131,7 @@ pa_status decode_impl(int stages, const pa_cache_desc* c, const void* key_cache,
   a.max_ctx = max_context_len;
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   a.stream_kv = (c->flags & PA_CACHE_SHARED_BLOCKS) == 0;
+  a.paged = paged;
 
   const DType dt = static_cast<DType>(c->dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -189,7 +197,7 @@ pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* v
                     int32_t num_q_heads, float scale, int32_t max_context_len,
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return decode_impl(kStageAttention | kStageReduce, c, key_cache, value_cache, out, query,
+  return decode_impl(kStageAttention | kStageReduce, true, c, key_cache, value_cache, out, query,
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
                      max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
@@ -200,7 +208,7 @@ pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                               float scale, int32_t max_context_len, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kStageAttention, c, key_cache, value_cache, out, query, block_tables,
+  return decode_impl(kStageAttention, true, c, key_cache, value_cache, out, query, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
                      max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
@@ -211,8 +219,19 @@ pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                            float scale, int32_t max_context_len, int32_t partition_size,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(kStageReduce, c, key_cache, value_cache, out, query, block_tables,
+  return decode_impl(kStageReduce, true, c, key_cache, value_cache, out, query, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                     max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
+                               const void* value_cache, void* out, const void* query,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, float scale,
+                               int32_t max_context_len, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return decode_impl(kStageAttention | kStageReduce, false, c, key_cache, value_cache, out, query,
+                     nullptr, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
                      max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
 

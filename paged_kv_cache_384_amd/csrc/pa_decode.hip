@@ -240,7 +240,7 @@ struct MfmaBlockStep {
   }
 };
 
-template <DType dt, int D, int NH, bool kStream>
+template <DType dt, int D, int NH, bool kStream, bool kPaged>
 __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
   using G = TileGeom<dt, D>;
   constexpr int kLoads = G::kLoads;
@@ -284,18 +284,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
 
   // ---- this wavefront's blocks ------------------------------------------------------------
-  // a contiguous range [jb, je) of the partition's blocks; their physical ids are wave-uniform
-  // and come straight from the table with scalar loads, clamped into [0, NB)
-  const int32_t* bt_row =
-      a.block_tables + static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
+  // a contiguous range [jb, je) of the partition's blocks. Paged: their physical ids are
+  // wave-uniform and come straight from the table with scalar loads ([anal] §3: the kernel
+  // looks each logical block up in the block table), clamped into [0, NB). The contiguous twin
+  // has no table: block j of sequence s is physical block s * max_blocks + j.
+  const int64_t row0 = static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
+  [[maybe_unused]] const int32_t* bt_row = a.block_tables + row0;
   const int per_wave = nblk / kWaves;
   const int extra = nblk % kWaves;
   const int jb = wave * per_wave + min(wave, extra);
   const int je = jb + per_wave + (wave < extra ? 1 : 0);
   const int num_blocks = a.num_blocks;
-  auto block_id = [&](int j) {
-    const int id = bt_row[j];
-    return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+  auto block_id = [&](int j) -> int {
+    if constexpr (kPaged) {
+      const int id = bt_row[j];
+      return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+    } else {
+      const int64_t id = row0 + j;
+      return id >= num_blocks ? num_blocks - 1 : static_cast<int>(id);
+    }
   };
 
   constexpr bool kMfma = use_mfma_scores<dt, D, NH>();
@@ -476,11 +483,15 @@ template <DType dt, int D, int NH>
 static hipError_t launch_attn(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n =
       static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.head_groups * a.num_parts;
-  if (a.stream_kv)
-    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true>), dim3(static_cast<unsigned>(n)),
-                       dim3(kDecodeThreads), 0, stream, a);
+  // contiguous sequences never share blocks, so the twin always streams
+  if (!a.paged)
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true, false>),
+                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
+  else if (a.stream_kv)
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true, true>),
+                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, false>),
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, false, true>),
                        dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -62,6 +62,8 @@ struct DecodeArgs {
   int32_t max_ctx;
   float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
   bool stream_kv;       // read key/value tiles with non-temporal (streaming) loads
+  bool paged;           // false: no table, sequence s's block j is physical block
+                        // s * max_blocks + j (the contiguous twin)
 };
 
 // Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).

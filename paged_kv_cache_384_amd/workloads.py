@@ -63,6 +63,9 @@ class DecodeConfig:
                                               are uniform in [lo, hi]
     ``num_blocks`` = 0 sizes the pool as ceil(pool_slack * blocks in use) + 1 (the extra block is
     the poison block that unused table entries point at).
+    ``placement``: "shuffled" hands physical blocks out in a seeded random order; "contiguous"
+    gives sequence s the span of physical blocks [s * W, s * W + ceil(ctx / B)) with W the
+    table width (the layout of a cache that is not paged; the pool is S * W + 1 blocks).
     """
     name: str
     dtype: str
@@ -77,6 +80,7 @@ class DecodeConfig:
     seed: int = 0
     partition_size: int = 0
     description: str = ""
+    placement: str = "shuffled"
 
     @property
     def esz(self) -> int:
@@ -310,10 +314,22 @@ def build_batch(cfg: DecodeConfig) -> DecodeBatch:
         ctx = _draw_context_lens(cfg, rng)
         suffix = None
         blocks_needed = int(sum(-(-int(c) // B) for c in ctx))
-    nb_pool = cfg.num_blocks or int(math.ceil(cfg.pool_slack * blocks_needed)) + 1
-    if nb_pool < blocks_needed + 1:
-        raise PoolExhausted(f"pool of {nb_pool} blocks cannot hold {blocks_needed} + poison")
-    bm = BlockManager(nb_pool, B, rng=rng)
+    maxb = max(1, -(-cfg.max_ctx_bound // B))
+    if cfg.placement == "contiguous":
+        if kind == "shared_prefix":
+            raise ValueError("a contiguous cache cannot share blocks")
+        S = cfg.num_seqs
+        nb_pool = S * maxb + 1
+        # hand-out order: the poison block (the last id) first, then each sequence's own span
+        spans = [np.arange(s * maxb, s * maxb + -(-int(c) // B)) for s, c in enumerate(ctx)]
+        used = np.concatenate([np.array([nb_pool - 1])] + spans)
+        rest = np.setdiff1d(np.arange(nb_pool), used)
+        bm = BlockManager(nb_pool, B, order=np.concatenate([used, rest]))
+    else:
+        nb_pool = cfg.num_blocks or int(math.ceil(cfg.pool_slack * blocks_needed)) + 1
+        if nb_pool < blocks_needed + 1:
+            raise PoolExhausted(f"pool of {nb_pool} blocks cannot hold {blocks_needed} + poison")
+        bm = BlockManager(nb_pool, B, rng=rng)
     poison = bm.take()
     if kind == "shared_prefix":
         prompt, lo, hi, n = cfg.ctx[1:]
@@ -333,7 +349,6 @@ def build_batch(cfg: DecodeConfig) -> DecodeBatch:
             bm.append_tokens(s, int(c))
             seqs.append(s)
     S = cfg.num_seqs
-    maxb = max(1, -(-cfg.max_ctx_bound // B))
     tables = np.full((S, maxb), poison, dtype=np.int32)
     for i, s in enumerate(seqs):
         t = bm.tables[s]

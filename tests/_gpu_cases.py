@@ -59,13 +59,15 @@ def same_bits(a: np.ndarray, b: np.ndarray, dtype: str) -> bool:
 
 
 def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=True,
-             check_pools=True, value_seed=0, shared_blocks=None):
+             check_pools=True, value_seed=0, shared_blocks=None, twin=False):
     """Run one step on the GPU and check it against the oracle.
 
     sample: None = every (seq, head) through the oracle; else a list of sequence ids whose
     outputs (all heads) the oracle computes.
     shared_blocks: the read-policy flag passed to pa_decode (None = whether the batch's tables
     share blocks).
+    twin: the batch is laid out contiguously; also run pa_decode_contiguous (no table) and
+    require it to give pa_decode's output bit for bit.
     Returns a dict of measured errors.
     """
     dev = torch.device("cuda:0")
@@ -120,6 +122,12 @@ def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=
     pa.pa_decode(out_d, q_d, kp_d, vp_d, bt_d, ctx_d, cfg.scale, batch.max_context_len,
                  partition_size, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
+    if twin:
+        out2_d = torch.full_like(q_d, float("nan"))
+        pa.pa_decode_contiguous(out2_d, q_d, kp_d, vp_d, ctx_d, cfg.scale, batch.max_context_len,
+                                batch.max_blocks_per_seq, partition_size)
+        torch.cuda.synchronize()
+        assert same_bits(to_storage(out2_d), to_storage(out_d), dt), "contiguous twin differs"
     out = to_storage(out_d)
     seqs = list(range(cfg.num_seqs)) if sample is None else list(sample)
     t1 = time.time()

@@ -110,6 +110,24 @@ def test_stage_entry_points_share_validation(L):
                   32, P(0), 0, P(0)) == WS
 
 
+def test_contiguous_twin_validation(L):
+    def dc(d=None, *, S=2, maxb=8, max_ctx=100, ptrs=None):
+        d = desc() if d is None else d
+        p = ptrs or {}
+        return L.pa_decode_contiguous(ctypes.byref(d) if d is not False else None,
+                                      p.get("k", GOOD), p.get("v", GOOD), p.get("out", GOOD),
+                                      p.get("q", GOOD), maxb, p.get("ctx", GOOD), S, 4, 0.1,
+                                      max_ctx, 0, P(0), 0, P(0))
+    assert dc(False) == NULL
+    assert dc(desc(flags=1)) == UNSUP                    # contiguous sequences share nothing
+    assert dc(desc(nb=15), maxb=8) == SHAPE              # 2 sequences x 8 blocks > 15
+    assert dc(max_ctx=8 * 16 + 1) == SHAPE
+    for k in ("k", "v", "out", "q", "ctx"):
+        assert dc(ptrs={k: P(0)}) == NULL, k
+    assert dc(ptrs={"q": ODD}) == ALIGN
+    assert dc(S=0, ptrs={k: P(0) for k in ("k", "v", "out", "q", "ctx")}) == OK
+
+
 def test_workspace_bytes(L):
     d = desc(dtype=2, hkv=8, d=128)
     # longest context fits the default partition: no workspace

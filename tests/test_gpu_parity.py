@@ -79,3 +79,22 @@ def test_all_empty():
                           head_dim=64, ctx=("fixed", (0, 0, 0)), seed=31)
     log("[parity] all contexts empty")
     run_step(cfg)
+
+
+TWIN = [
+    ("tiny_fp32", dict(placement="contiguous")),
+    ("opt13b_fp16", dict(num_seqs=6, num_q_heads=5, num_kv_heads=5, ctx=("uniform", 1, 700),
+                         placement="contiguous")),
+    ("gqa_bf16", dict(num_seqs=8, num_q_heads=16, num_kv_heads=4,
+                      ctx=("lognormal", 200, 0.75, 1, 1200), placement="contiguous")),
+]
+
+
+@pytest.mark.parametrize("name,over", TWIN, ids=[c[0] for c in TWIN])
+def test_contiguous_twin(name, over):
+    """The contiguous twin (no block table) matches the oracle and pa_decode bit for bit over a
+    cache laid out contiguously."""
+    cfg = wl.config(name, **over)
+    for part in (0, 64):
+        log(f"[parity] contiguous twin {name} partition={part}")
+        run_step(cfg, partition_size=part, twin=True)

@@ -170,3 +170,28 @@ def test_kv_bytes_accounting():
     assert b.kv_bytes() == int(b.context_lens.sum()) * 40 * 128 * 2 * 2
     # expected value: 64 seqs * mean ctx 1088 * 40 heads * 128 * 2 (K and V) * 2 bytes = 1.43 GB
     assert abs(b.kv_bytes() / 1.426e9 - 1) < 0.1
+
+
+def test_contiguous_placement_gives_each_sequence_its_own_span():
+    """placement="contiguous": sequence s holds physical blocks s*W .. s*W + ceil(ctx/B) - 1 in
+    order (W = table width), unused entries point at the poison block (the last id), and the
+    context lengths are those of the shuffled batch of the same seed."""
+    for name in ("opt13b_fp16", "gqa_bf16", "tiny_fp32"):
+        cfg = wl.config(name, placement="contiguous")
+        b = wl.build_batch(cfg)
+        S, W = b.block_tables.shape
+        assert b.num_blocks == S * W + 1 and b.poison_block == S * W
+        for s in range(S):
+            nb = -(-int(b.context_lens[s]) // cfg.block_size)
+            assert np.array_equal(b.block_tables[s, :nb], s * W + np.arange(nb))
+            assert (b.block_tables[s, nb:] == b.poison_block).all()
+        assert not b.shares_blocks
+        assert np.array_equal(b.context_lens, wl.build_batch(wl.CONFIGS[name]).context_lens)
+    with pytest.raises(ValueError):
+        wl.build_batch(wl.config("cow_fp16", placement="contiguous"))
+
+
+def test_shares_blocks_flags_only_the_shared_prefix_workload():
+    assert wl.build_batch(wl.CONFIGS["cow_fp16"]).shares_blocks
+    for name in ("tiny_fp32", "opt13b_fp16", "gqa_bf16", "long_bf16"):
+        assert not wl.build_batch(wl.CONFIGS[name]).shares_blocks
