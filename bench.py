@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["paged_kv_cache_384_amd/csrc/pa_decode.hip",
+KERNEL_SOURCES = ["paged_kv_cache_384_amd/csrc/pa_attention.h",
                   "paged_kv_cache_384_amd/csrc/pa_device.h"]
 
 
@@ -163,6 +163,9 @@ def main():
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition size in tokens; -1 = the workload's own setting")
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="run the workload at this block size (8, 16 or 32) instead of its own; "
+                         "the pool is then sized for the blocks in use (1.25x)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -189,6 +192,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     cfg = wl.CONFIGS[args.config]
+    if args.block_size and args.block_size != cfg.block_size:
+        cfg = wl.config(args.config, block_size=args.block_size, num_blocks=0)
     part = cfg.partition_size if args.partition < 0 else args.partition
     batch = wl.build_batch(cfg)
     print(f"[bench] {cfg.name}: {cfg.description}", file=sys.stderr, flush=True)

@@ -33,14 +33,17 @@
  *                element (t, i) at   (i / W) * (block_size * W) + t * W + (i % W)
  *
  * i.e. the key tile is cut into head_dim / W chunk rows; chunk row c holds the W elements
- * [c*W, c*W + W) of slot 0, then of slot 1, ... of slot block_size-1. At block_size 16 a chunk
- * row is 1 KiB, so one 64-lane wavefront loading 16 bytes per lane reads a whole chunk row in one
- * fully coalesced instruction, and each group of four lanes holds 64 contiguous bytes of one
- * token. A tile is 4 KiB in every supported configuration with 256-byte token rows
- * (head_dim 128 at 16-bit, head_dim 64 at 32-bit).
+ * [c*W, c*W + W) of slot 0, then of slot 1, ... of slot block_size-1 (64 bytes per slot). Any
+ * 16 consecutive slots of a chunk row are 1 KiB, so one 64-lane wavefront loading 16 bytes per
+ * lane reads them in one fully coalesced instruction, each group of four lanes holding 64
+ * contiguous bytes of one token: a chunk row is that 1 KiB at block_size 16, two of them at 32,
+ * and half of one at 8 (the two halves of a wave load then come from two blocks). A tile is
+ * block_size * 256 bytes in every configuration with 256-byte token rows (head_dim 128 at
+ * 16-bit, head_dim 64 at 32-bit).
  *
  * Supported: dtype PA_F32 / PA_F16 / PA_BF16 (query, new keys/values, pools and output share
- * it), head_dim 64 or 128, block_size 16.
+ * it), head_dim 64 or 128, block_size 8, 16 or 32 ([anal] §6 and [dev]: 16 is the default; the
+ * block size trades table lookups against the up to B-1 slots a sequence's last block wastes).
  */
 #ifndef PA_H
 #define PA_H
@@ -61,7 +64,7 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
-  PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim or block_size the kernels are not built for */
+  PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim, block_size or flag the kernels do not support */
   PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned (int arrays: 4-byte) */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_decode_workspace_bytes() */
   PA_ERR_LAUNCH = 6,      /* the HIP runtime reported an error when launching */
@@ -135,7 +138,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32
  * n = 0 writes zeros. Accumulation is fp32; out is rounded to c->dtype (nearest even).
  *
  * Contexts longer than one partition are split into partitions of partition_size tokens
- * (a multiple of B, at most PA_MAX_PARTITION_TOKENS; 0 = library choice). Each partition keeps
+ * (a multiple of 16 and of B, at most PA_MAX_PARTITION_TOKENS; 0 = library choice). Each partition keeps
  * its softmax state (running max m, sum l, unnormalised output) in the workspace, and a second
  * kernel merges the states of each (sequence, head) with the usual max-rescaling.
  *

@@ -11,7 +11,8 @@ kernels; there is no fallback. If the library is not built, the first call raise
     pa_copy_blocks(key_cache, value_cache, src_dst)
 
 Pools are tensors of shape [num_blocks, num_kv_heads, block_size * head_dim] in the element
-dtype; the order of elements inside each (block, head) tile is the library's (see pa.h).
+dtype; the order of elements inside each (block, head) tile is the library's (see pa.h). The
+block size (8, 16 or 32) is read off the pool shape unless passed as ``block_size``.
 """
 from __future__ import annotations
 
@@ -125,8 +126,13 @@ def _stream(t, stream):
     return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _desc(key_cache, head_dim, block_size, shared_blocks=False) -> CacheDesc:
-    if key_cache.dim() != 3 or key_cache.shape[2] != block_size * head_dim:
+def _desc(key_cache, head_dim, block_size=None, shared_blocks=False) -> CacheDesc:
+    """The pools' descriptor; the block size is read off the pool shape unless given."""
+    if key_cache.dim() != 3 or key_cache.shape[2] % head_dim:
+        raise ValueError("pools must be [num_blocks, num_kv_heads, block_size * head_dim]")
+    if block_size is None:
+        block_size = key_cache.shape[2] // head_dim
+    if key_cache.shape[2] != block_size * head_dim:
         raise ValueError("pools must be [num_blocks, num_kv_heads, block_size * head_dim]")
     return CacheDesc(DTYPE_CODES[_dtype_name(key_cache)], key_cache.shape[0], key_cache.shape[1],
                      head_dim, block_size, CACHE_SHARED_BLOCKS if shared_blocks else 0)
@@ -140,7 +146,7 @@ def _check(status: int, where: str) -> None:
 # ---- the calls ----------------------------------------------------------------------------
 
 def pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token_seq, token_pos,
-                         *, block_size: int = 16, stream=None) -> None:
+                         *, block_size: int | None = None, stream=None) -> None:
     """Write key[n] / value[n] ([T, Hkv, d]) into the slot of (token_seq[n], token_pos[n])."""
     import torch
     head_dim = key.shape[-1]
@@ -163,7 +169,7 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token
 
 def pa_decode_workspace_bytes(key_cache, num_seqs: int, num_q_heads: int, head_dim: int,
                               max_context_len: int, partition_size: int = 0,
-                              block_size: int = 16) -> int:
+                              block_size: int | None = None) -> int:
     d = _desc(key_cache, head_dim, block_size)
     n = lib().pa_decode_workspace_bytes(ctypes.byref(d), num_seqs, num_q_heads, max_context_len,
                                         partition_size)
@@ -200,8 +206,8 @@ def _decode_call(fn_name, out, query, key_cache, value_cache, block_tables, cont
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-              max_context_len, partition_size: int = 0, workspace=None, *, block_size: int = 16,
-              shared_blocks: bool = False, stream=None):
+              max_context_len, partition_size: int = 0, workspace=None, *,
+              block_size: int | None = None, shared_blocks: bool = False, stream=None):
     """out[s, h] = attention of query[s, h] over sequence s's paged cache (both stages).
 
     shared_blocks: some physical blocks are referenced by several sequences in this call, so the
@@ -215,7 +221,7 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
 
 def pa_decode_attention(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                         max_context_len, partition_size: int = 0, workspace=None, *,
-                        block_size: int = 16, shared_blocks: bool = False, stream=None):
+                        block_size: int | None = None, shared_blocks: bool = False, stream=None):
     """First stage of pa_decode only (per-partition attention)."""
     return _decode_call("pa_decode_attention", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
@@ -224,7 +230,7 @@ def pa_decode_attention(out, query, key_cache, value_cache, block_tables, contex
 
 def pa_decode_reduce(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                      max_context_len, partition_size: int = 0, workspace=None, *,
-                     block_size: int = 16, shared_blocks: bool = False, stream=None):
+                     block_size: int | None = None, shared_blocks: bool = False, stream=None):
     """Second stage of pa_decode only (merge of partition states)."""
     return _decode_call("pa_decode_reduce", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
@@ -233,7 +239,7 @@ def pa_decode_reduce(out, query, key_cache, value_cache, block_tables, context_l
 
 def pa_decode_contiguous(out, query, key_cache, value_cache, context_lens, scale, max_context_len,
                          max_blocks_per_seq, partition_size: int = 0, workspace=None, *,
-                         block_size: int = 16, stream=None):
+                         block_size: int | None = None, stream=None):
     """The contiguous twin of pa_decode: sequence s's block j is physical block
     s * max_blocks_per_seq + j (no block table). Returns the workspace used."""
     import torch
@@ -258,7 +264,7 @@ def pa_decode_contiguous(out, query, key_cache, value_cache, context_lens, scale
     return workspace
 
 
-def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int = 16,
+def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int | None = None,
                    stream=None) -> None:
     """Copy block src_dst[k, 0] onto block src_dst[k, 1] in both pools."""
     import torch

@@ -21,7 +21,7 @@ pa_status check_desc(const pa_cache_desc* c) {
   if (c == nullptr) return PA_ERR_NULL;
   if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (c->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32) return PA_ERR_UNSUPPORTED;
   if ((c->flags & ~PA_CACHE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
   return PA_OK;
@@ -31,16 +31,22 @@ int64_t tile_bytes(const pa_cache_desc* c) {
   return static_cast<int64_t>(c->block_size) * c->head_dim * elem_size(c->dtype);
 }
 
+// Partitions are whole 16-token groups and whole blocks: multiples of max(16, B).
+int32_t partition_quantum(const pa_cache_desc* c) {
+  return c->block_size > pa::kGroupTokens ? c->block_size : pa::kGroupTokens;
+}
+
 // Partition size when the caller passes 0. One partition when the longest context fits in
-// 512 tokens; otherwise 512-token partitions (32 blocks: eight per wavefront), which keeps
+// 512 tokens; otherwise 512-token partitions (32 groups: eight per wavefront), which keeps
 // every workgroup's key/value stream long enough to amortise its setup while giving the
 // launch enough independent workgroups for 256 CUs.
-int32_t choose_partition(int32_t max_context_len, int32_t requested) {
+int32_t choose_partition(const pa_cache_desc* c, int32_t max_context_len, int32_t requested) {
   if (requested > 0) return requested;
   constexpr int32_t kDefault = 512;
+  const int32_t q = partition_quantum(c);
   if (max_context_len <= kDefault) {
-    const int32_t p = (max_context_len + pa::kBlockSize - 1) / pa::kBlockSize * pa::kBlockSize;
-    return p < pa::kBlockSize ? pa::kBlockSize : p;
+    const int32_t p = (max_context_len + q - 1) / q * q;
+    return p < q ? q : p;
   }
   return kDefault;
 }
@@ -58,10 +64,10 @@ pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_he
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
   if (max_context_len < 0) return PA_ERR_SHAPE;
-  if (partition_size < 0 || partition_size % c->block_size != 0 ||
+  if (partition_size < 0 || partition_size % partition_quantum(c) != 0 ||
       partition_size > pa::kMaxPartitionTokens)
     return PA_ERR_SHAPE;
-  const int32_t part = choose_partition(max_context_len, partition_size);
+  const int32_t part = choose_partition(c, max_context_len, partition_size);
   const int32_t np = max_context_len <= part ? 1 : (max_context_len + part - 1) / part;
   const int32_t group = num_q_heads / c->num_kv_heads;
   const int32_t nh = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
@@ -136,7 +142,13 @@ pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void
   const DType dt = static_cast<DType>(c->dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stages & kStageAttention) {
-    if (pa::launch_decode_attention(dt, c->head_dim, a, s) != hipSuccess) return PA_ERR_LAUNCH;
+    hipError_t e;
+    switch (c->block_size) {
+      case 8: e = pa::launch_decode_attention_b8(dt, c->head_dim, a, s); break;
+      case 32: e = pa::launch_decode_attention_b32(dt, c->head_dim, a, s); break;
+      default: e = pa::launch_decode_attention_b16(dt, c->head_dim, a, s); break;
+    }
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (stages & kStageReduce) {
     if (pa::launch_decode_reduce(dt, c->head_dim, a, s) != hipSuccess) return PA_ERR_LAUNCH;
@@ -177,7 +189,7 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* va
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = c->num_blocks;
   a.num_kv_heads = c->num_kv_heads;
-  if (pa::launch_reshape_and_cache(static_cast<DType>(c->dtype), c->head_dim, a,
+  if (pa::launch_reshape_and_cache(static_cast<DType>(c->dtype), c->head_dim, c->block_size, a,
                                    static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;

@@ -1,4 +1,5 @@
-// Decode attention over the paged KV cache (the partition merge is in pa_reduce.hip).
+// Decode attention over the paged KV cache: the kernel template, instantiated per block size in
+// pa_attention_b8.hip / _b16.hip / _b32.hip (the partition merge is in pa_reduce.hip).
 //
 // Sources (page title, section):
 //   "PagedAttention" (newikis.com), "수학적 공식": dense causal attention of the newest token
@@ -9,9 +10,13 @@
 //   output, one division at the end); the result equals ordinary attention.
 //
 // Work decomposition (gfx950): one 256-thread workgroup (four wavefronts) per
-// (KV head, sequence, query-head group, context partition). The partition's block-table slice
-// is staged in LDS; wavefront w then streams blocks w, w+4, w+8, ... of the partition in a
-// single pass over keys and values:
+// (KV head, sequence, query-head group, context partition). The unit of work inside a partition
+// is a group of 16 consecutive tokens, whatever the block size B: one 64-lane wave load of 16
+// bytes per lane covers 16 tokens of a key chunk row (1 KiB at 64 bytes per token). At B = 16 a
+// group is one block; at B = 32 a block holds two groups (its chunk rows are 2 KiB, the second
+// group starts 1 KiB in); at B = 8 a group spans two blocks, lanes 0-31 and 32-63 addressing
+// different physical blocks. Wavefront w streams a contiguous quarter of the partition's groups
+// in a single pass over keys and values:
 //   * keys: kLoads 16-byte loads per lane, each reading one whole 1 KiB key chunk row, so lane l
 //     holds 64 contiguous bytes of token l/4 per row; dot2 instructions against the query piece
 //     the lane keeps in registers and a two-step DPP quad sum give every token's score in the
@@ -30,6 +35,8 @@
 // unnormalised output) for the merge kernel. Only the last block of a partition can hold slots
 // past the context end; those are masked with selects (score -inf, value 0) so stale or NaN
 // contents never enter the result.
+#pragma once
+
 #include <utility>
 
 #include "pa_device.h"
@@ -59,27 +66,31 @@ struct RowWeights {
   }
 };
 
-// One block of one wavefront's stream: scores, running-softmax update, weighted values.
-// kPrefetch: the block is full and its registers are refilled with the block at byte offset
-// offn as soon as the keys and then the values are consumed. Otherwise the block may be the
-// partition's last, so slots at or past len are masked, and nothing is loaded.
-template <DType dt, int D, int NH, bool kStream, bool kPrefetch>
+// This lane's addresses of one 16-token group's key and value pieces: key piece c at
+// k + c * (B * 64), value piece i at v + i * row bytes.
+struct GroupPtrs {
+  const uint8_t* k;
+  const uint8_t* v;
+};
+
+// One 16-token group of one wavefront's stream: scores, running-softmax update, weighted values.
+// kPrefetch: the group is full and its registers are refilled with the group at `next` as soon
+// as the keys and then the values are consumed. Otherwise the group may be the partition's last,
+// so slots at or past len are masked, and nothing is loaded.
+template <DType dt, int D, int B, int NH, bool kStream, bool kPrefetch>
 struct BlockStep {
-  using G = TileGeom<dt, D>;
+  using G = TileGeom<dt, D, B>;
   static constexpr int kLoads = G::kLoads;
   static constexpr int kEpp = G::kEpp;
   static constexpr int kPiecesPerRow = G::kPiecesPerRow;
 
   const u32x4 (&qv)[NH][kLoads];
-  const uint8_t* kbase;
-  const uint8_t* vbase;
-  int64_t tile_stride;
   float scale_log2;
   int lane;
   int vrow0;
   int len;
 
-  __device__ __forceinline__ void run(int j, int64_t offn, u32x4 (&kb)[kLoads],
+  __device__ __forceinline__ void run(int g, GroupPtrs next, u32x4 (&kb)[kLoads],
                                       u32x4 (&vb)[kLoads], float (&m)[NH], float (&lsum)[NH],
                                       float (&acc)[NH][kEpp]) const {
     float sc[NH];
@@ -92,9 +103,10 @@ struct BlockStep {
     }
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + offn + c * 1024);
+      for (int c = 0; c < kLoads; ++c)
+        kb[c] = load16_kv<kStream>(next.k + c * G::kChunkRowBytes);
     } else {
-      const bool valid = j * kBlockSize + (lane >> 2) < len;
+      const bool valid = g * kGroupTokens + (lane >> 2) < len;
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) sc[hh] = valid ? sc[hh] : -INFINITY;
     }
@@ -121,7 +133,7 @@ struct BlockStep {
       float v[kEpp];
       Widen<dt>::run(vb[i], v);
       if constexpr (!kPrefetch) {
-        if (j * kBlockSize + vrow0 + i >= len) {
+        if (g * kGroupTokens + vrow0 + i >= len) {
 #pragma unroll
           for (int e = 0; e < kEpp; ++e) v[e] = 0.0f;
         }
@@ -133,7 +145,7 @@ struct BlockStep {
     }
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + offn + i * G::kRowBytes);
+      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
     }
   }
 };
@@ -155,17 +167,14 @@ constexpr bool use_mfma_scores() {
 // tokens 4(l/16) .. 4(l/16)+3, which are the value rows its own row of 16 lanes accumulates, so
 // lane 16r + h hands head h's weights to its row with DPP row broadcasts. The running maximum m
 // and sum lsum are per lane, for head l%16 (equal in the four rows once reduced).
-template <DType dt, int NH, bool kStream, bool kPrefetch>
+template <DType dt, int B, int NH, bool kStream, bool kPrefetch>
 struct MfmaBlockStep {
-  using G = TileGeom<dt, 128>;
+  using G = TileGeom<dt, 128, B>;
   static constexpr int kLoads = G::kLoads;
   static constexpr int kEpp = G::kEpp;
-  static_assert(kLoads == 4 && G::kPiecesPerRow == 16, "256-byte rows at block size 16");
+  static_assert(kLoads == 4 && G::kPiecesPerRow == 16, "256-byte rows");
 
   const u32x4 (&qm)[kLoads];
-  const uint8_t* kbase;
-  const uint8_t* vbase;
-  int64_t tile_stride;
   float scale_log2;
   int lane;
   int vrow0;
@@ -177,7 +186,7 @@ struct MfmaBlockStep {
     ((out[H] = row_bcast<H>(x)), ...);
   }
 
-  __device__ __forceinline__ void run(int j, int64_t offn, u32x4 (&kb)[kLoads],
+  __device__ __forceinline__ void run(int g, GroupPtrs next, u32x4 (&kb)[kLoads],
                                       u32x4 (&vb)[kLoads], float& m, float& lsum,
                                       float (&acc)[NH][kEpp]) const {
     f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -185,14 +194,15 @@ struct MfmaBlockStep {
     for (int c = 0; c < kLoads; ++c) d = Mfma16x16x32<dt>::run(kb[c], qm[c], d);
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) kb[c] = load16_kv<kStream>(kbase + offn + c * 1024);
+      for (int c = 0; c < kLoads; ++c)
+        kb[c] = load16_kv<kStream>(next.k + c * G::kChunkRowBytes);
     }
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = d[i] * scale_log2;
     if constexpr (!kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = j * kBlockSize + vrow0 + i < len ? sc[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) sc[i] = g * kGroupTokens + vrow0 + i < len ? sc[i] : -INFINITY;
     }
 
     float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -223,7 +233,7 @@ struct MfmaBlockStep {
       float v[kEpp];
       Widen<dt>::run(vb[i], v);
       if constexpr (!kPrefetch) {
-        if (j * kBlockSize + vrow0 + i >= len) {
+        if (g * kGroupTokens + vrow0 + i >= len) {
 #pragma unroll
           for (int e = 0; e < kEpp; ++e) v[e] = 0.0f;
         }
@@ -235,14 +245,14 @@ struct MfmaBlockStep {
     }
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(vbase + offn + i * G::kRowBytes);
+      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
     }
   }
 };
 
-template <DType dt, int D, int NH, bool kStream, bool kPaged>
+template <DType dt, int D, int B, int NH, bool kStream, bool kPaged>
 __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
-  using G = TileGeom<dt, D>;
+  using G = TileGeom<dt, D, B>;
   constexpr int kLoads = G::kLoads;
   constexpr int kEpp = G::kEpp;
   constexpr int kPiecesPerRow = G::kPiecesPerRow;
@@ -280,18 +290,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   const int start = part * a.part_tokens;
   if (start >= ctx) return;
   const int len = min(a.part_tokens, ctx - start);
-  const int nblk = (len + kBlockSize - 1) / kBlockSize;
+  const int ngroups = (len + kGroupTokens - 1) / kGroupTokens;  // 16-token groups
+  const int nblocks = (len + B - 1) / B;                         // table entries this partition
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
 
-  // ---- this wavefront's blocks ------------------------------------------------------------
-  // a contiguous range [jb, je) of the partition's blocks. Paged: their physical ids are
-  // wave-uniform and come straight from the table with scalar loads ([anal] §3: the kernel
-  // looks each logical block up in the block table), clamped into [0, NB). The contiguous twin
-  // has no table: block j of sequence s is physical block s * max_blocks + j.
-  const int64_t row0 = static_cast<int64_t>(s) * a.max_blocks + start / kBlockSize;
+  // ---- this wavefront's groups -------------------------------------------------------------
+  // a contiguous range [jb, je) of the partition's groups. Paged: the physical ids of their
+  // blocks are wave-uniform and come straight from the table with scalar loads ([anal] §3: the
+  // kernel looks each logical block up in the block table), clamped into [0, NB). The
+  // contiguous twin has no table: block j of sequence s is physical block s * max_blocks + j.
+  const int64_t row0 = static_cast<int64_t>(s) * a.max_blocks + start / B;
   [[maybe_unused]] const int32_t* bt_row = a.block_tables + row0;
-  const int per_wave = nblk / kWaves;
-  const int extra = nblk % kWaves;
+  const int per_wave = ngroups / kWaves;
+  const int extra = ngroups % kWaves;
   const int jb = wave * per_wave + min(wave, extra);
   const int je = jb + per_wave + (wave < extra ? 1 : 0);
   const int num_blocks = a.num_blocks;
@@ -308,14 +319,37 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   constexpr bool kMfma = use_mfma_scores<dt, D, NH>();
   const int64_t tile_stride = static_cast<int64_t>(a.num_kv_heads) * G::kTileBytes;
   const uint8_t* qbase = a.query + (static_cast<int64_t>(s) * a.num_q_heads + h0) * G::kRowBytes;
-  // key piece c of a lane: VALU scores read byte 16*l of chunk row c (token l/4); matrix-core
-  // scores read byte 64*(l%16) + 16*(l/16) (token l%16)
-  const uint8_t* kbase = a.k_pool + static_cast<int64_t>(kvh) * G::kTileBytes +
-                         (kMfma ? 64 * (lane & 15) + 16 * (lane >> 4) : 16 * lane);
-  // value piece i of a lane: row vrow0 + i, bytes [(lane % kPiecesPerRow) * 16, +16)
+  // the token of the group a lane's key pieces belong to: VALU scores read byte 16*l of each
+  // 16-token chunk-row segment (token l/4), matrix-core scores read byte 64*(l%16) + 16*(l/16)
+  // (token l%16); its value rows are vrow0 + i, bytes [(lane % kPiecesPerRow) * 16, +16)
+  const int ktok = kMfma ? (lane & 15) : (lane >> 2);
+  const int kbyte = kMfma ? 64 * (lane & 15) + 16 * (lane >> 4) : 16 * lane;
   const int vrow0 = (lane / kPiecesPerRow) * kLoads;
-  const uint8_t* vbase = a.v_pool + static_cast<int64_t>(kvh) * G::kTileBytes +
-                         vrow0 * G::kRowBytes + (lane % kPiecesPerRow) * 16;
+  const int vbyte = (lane % kPiecesPerRow) * 16;
+  const uint8_t* kpool = a.k_pool + static_cast<int64_t>(kvh) * G::kTileBytes;
+  const uint8_t* vpool = a.v_pool + static_cast<int64_t>(kvh) * G::kTileBytes;
+  // this lane's addresses for group gg
+  auto group_ptrs = [&](int gg) -> GroupPtrs {
+    if constexpr (B >= kGroupTokens) {
+      // block gg / (B/16) holds the group; its tokens start at slot 16 * (gg % (B/16))
+      constexpr int kPer = B / kGroupTokens;
+      const int64_t base = block_id(gg / kPer) * tile_stride;
+      const int sub = gg % kPer;
+      return {kpool + base + sub * (kGroupTokens * 64) + kbyte,
+              vpool + base + (sub * kGroupTokens + vrow0) * G::kRowBytes + vbyte};
+    } else {
+      // the group spans blocks 2gg (tokens 0-7) and 2gg + 1 (tokens 8-15); past the
+      // partition's last block the second is never scored, so its id is not looked up
+      static_assert(B * 2 == kGroupTokens, "block sizes 8, 16 and 32");
+      const int ja = 2 * gg;
+      const int ida = block_id(ja);
+      const int idb = ja + 1 < nblocks ? block_id(ja + 1) : ida;
+      const int kh = ktok / B;
+      const int vh = vrow0 / B;
+      return {kpool + (kh ? idb : ida) * tile_stride + (ktok - kh * B) * 64 + (kbyte & 63),
+              vpool + (vh ? idb : ida) * tile_stride + (vrow0 - vh * B) * G::kRowBytes + vbyte};
+    }
+  };
   const float scale_log2 = a.scale_log2;
 
   float acc[NH][kEpp];
@@ -359,11 +393,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   u32x4 kA[kLoads], vA[kLoads];
   [[maybe_unused]] u32x4 kB[kLoads], vB[kLoads];
   auto load_block = [&](int jj, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads]) {
-    const int64_t off = block_id(jj < je ? jj : nblk - 1) * tile_stride;
+    const GroupPtrs p = group_ptrs(jj < je ? jj : ngroups - 1);
 #pragma unroll
-    for (int c = 0; c < kLoads; ++c) kr[c] = load16_kv<kStream>(kbase + off + c * 1024);
+    for (int c = 0; c < kLoads; ++c) kr[c] = load16_kv<kStream>(p.k + c * G::kChunkRowBytes);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) vr[i] = load16_kv<kStream>(vbase + off + i * G::kRowBytes);
+    for (int i = 0; i < kLoads; ++i) vr[i] = load16_kv<kStream>(p.v + i * G::kRowBytes);
   };
   load_block(jb, kA, vA);
   if constexpr (kDepth == 2) load_block(jb + 1, kB, vB);
@@ -372,35 +406,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   auto stream_blocks = [&](auto& full, auto& tail, auto&... state) {
     int j = jb;
     if constexpr (kDepth == 1) {
-      for (; j + 1 < je; ++j) full.run(j, block_id(j + 1) * tile_stride, kA, vA, state...);
-      if (j < je) tail.run(j, 0, kA, vA, state...);
+      for (; j + 1 < je; ++j) full.run(j, group_ptrs(j + 1), kA, vA, state...);
+      if (j < je) tail.run(j, GroupPtrs{}, kA, vA, state...);
     } else {
       // pairs of full steps while at least four blocks remain (kA holds block j, kB block
       // j + 1 at the top of each pair), then the last one to three blocks
       for (; j + 3 < je; j += 2) {
-        full.run(j, block_id(j + 2) * tile_stride, kA, vA, state...);
-        full.run(j + 1, block_id(j + 3) * tile_stride, kB, vB, state...);
+        full.run(j, group_ptrs(j + 2), kA, vA, state...);
+        full.run(j + 1, group_ptrs(j + 3), kB, vB, state...);
       }
       const int left = je - j;
       if (left == 3) {
-        full.run(j, block_id(j + 2) * tile_stride, kA, vA, state...);
-        tail.run(j + 1, 0, kB, vB, state...);
-        tail.run(j + 2, 0, kA, vA, state...);
+        full.run(j, group_ptrs(j + 2), kA, vA, state...);
+        tail.run(j + 1, GroupPtrs{}, kB, vB, state...);
+        tail.run(j + 2, GroupPtrs{}, kA, vA, state...);
       } else if (left == 2) {
-        tail.run(j, 0, kA, vA, state...);
-        tail.run(j + 1, 0, kB, vB, state...);
+        tail.run(j, GroupPtrs{}, kA, vA, state...);
+        tail.run(j + 1, GroupPtrs{}, kB, vB, state...);
       } else if (left == 1) {
-        tail.run(j, 0, kA, vA, state...);
+        tail.run(j, GroupPtrs{}, kA, vA, state...);
       }
     }
   };
 
   if constexpr (kMfma) {
     float m = -INFINITY, lsum = 0.0f;
-    MfmaBlockStep<dt, NH, kStream, true> full{qm, kbase, vbase, tile_stride, scale_log2, lane,
-                                              vrow0, len};
-    MfmaBlockStep<dt, NH, kStream, false> tail{qm, kbase, vbase, tile_stride, scale_log2, lane,
-                                               vrow0, len};
+    MfmaBlockStep<dt, B, NH, kStream, true> full{qm, scale_log2, lane, vrow0, len};
+    MfmaBlockStep<dt, B, NH, kStream, false> tail{qm, scale_log2, lane, vrow0, len};
     stream_blocks(full, tail, m, lsum, acc);
     // lane h (< NH) of any row holds head h's maximum; its sum is spread over the four rows
     lsum += __shfl_xor(lsum, 16, 64);
@@ -416,10 +448,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
       m[hh] = -INFINITY;
       lsum[hh] = 0.0f;
     }
-    BlockStep<dt, D, NH, kStream, true> full{qv, kbase, vbase, tile_stride, scale_log2, lane,
-                                             vrow0, len};
-    BlockStep<dt, D, NH, kStream, false> tail{qv, kbase, vbase, tile_stride, scale_log2, lane,
-                                              vrow0, len};
+    BlockStep<dt, D, B, NH, kStream, true> full{qv, scale_log2, lane, vrow0, len};
+    BlockStep<dt, D, B, NH, kStream, false> tail{qv, scale_log2, lane, vrow0, len};
     stream_blocks(full, tail, m, lsum, acc);
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -477,43 +507,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
 }
 
 // ------------------------------------------------------------------------------------------
-// launchers
+// launch helpers (each pa_attention_b*.hip instantiates them for one block size)
 // ------------------------------------------------------------------------------------------
-template <DType dt, int D, int NH>
-static hipError_t launch_attn(const DecodeArgs& a, hipStream_t stream) {
+template <DType dt, int D, int B, int NH>
+hipError_t launch_attn(const DecodeArgs& a, hipStream_t stream) {
   const int64_t n =
       static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.head_groups * a.num_parts;
+  const dim3 grid(static_cast<unsigned>(n)), block(kDecodeThreads);
   // contiguous sequences never share blocks, so the twin always streams
   if (!a.paged)
-    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true, false>),
-                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, B, NH, true, false>), grid, block, 0,
+                       stream, a);
   else if (a.stream_kv)
-    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, true, true>),
-                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, B, NH, true, true>), grid, block, 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((decode_attention_kernel<dt, D, NH, false, true>),
-                       dim3(static_cast<unsigned>(n)), dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_attention_kernel<dt, D, B, NH, false, true>), grid, block, 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <DType dt, int D>
-static hipError_t launch_attn_nh(const DecodeArgs& a, hipStream_t stream) {
+template <DType dt, int D, int B>
+hipError_t launch_attn_nh(const DecodeArgs& a, hipStream_t stream) {
   switch (a.heads_per_wg) {
-    case 4: return launch_attn<dt, D, 4>(a, stream);
-    case 2: return launch_attn<dt, D, 2>(a, stream);
-    default: return launch_attn<dt, D, 1>(a, stream);
+    case 4: return launch_attn<dt, D, B, 4>(a, stream);
+    case 2: return launch_attn<dt, D, B, 2>(a, stream);
+    default: return launch_attn<dt, D, B, 1>(a, stream);
   }
 }
 
-hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
-                                   hipStream_t stream) {
+template <int B>
+hipError_t launch_attn_block(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream) {
   switch (dt) {
-    case DType::F32: return head_dim == 64 ? launch_attn_nh<DType::F32, 64>(a, stream)
-                                           : launch_attn_nh<DType::F32, 128>(a, stream);
-    case DType::F16: return head_dim == 64 ? launch_attn_nh<DType::F16, 64>(a, stream)
-                                           : launch_attn_nh<DType::F16, 128>(a, stream);
-    case DType::BF16: return head_dim == 64 ? launch_attn_nh<DType::BF16, 64>(a, stream)
-                                            : launch_attn_nh<DType::BF16, 128>(a, stream);
+    case DType::F32: return head_dim == 64 ? launch_attn_nh<DType::F32, 64, B>(a, stream)
+                                           : launch_attn_nh<DType::F32, 128, B>(a, stream);
+    case DType::F16: return head_dim == 64 ? launch_attn_nh<DType::F16, 64, B>(a, stream)
+                                           : launch_attn_nh<DType::F16, 128, B>(a, stream);
+    case DType::BF16: return head_dim == 64 ? launch_attn_nh<DType::BF16, 64, B>(a, stream)
+                                            : launch_attn_nh<DType::BF16, 128, B>(a, stream);
   }
   return hipErrorInvalidValue;
 }

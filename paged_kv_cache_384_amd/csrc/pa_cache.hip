@@ -14,16 +14,16 @@ namespace pa {
 // elements [q*Epp, q*Epp + Epp) of that head's vector. In the value tile it goes to row `slot`,
 // byte q*16; in the key tile to chunk row q/4 (64-byte chunks = 4 pieces), slot `slot`, byte
 // (q%4)*16 of that slot's 64-byte segment.
-template <DType dt, int D>
+template <DType dt, int D, int B>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
-  using G = TileGeom<dt, D>;
+  using G = TileGeom<dt, D, B>;
   const int n = blockIdx.x;
   const int s = a.token_seq[n];
   const int pos = a.token_pos[n];
-  if (pos < 0 || pos >= a.max_blocks * kBlockSize || s < 0 || s >= a.num_seqs) return;
-  int blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + pos / kBlockSize];
+  if (pos < 0 || pos >= a.max_blocks * B || s < 0 || s >= a.num_seqs) return;
+  int blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + pos / B];
   blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-  const int slot = pos % kBlockSize;
+  const int slot = pos % B;
   constexpr int kPieces = G::kPiecesPerRow;
   const int total = a.num_kv_heads * kPieces;
   for (int i = threadIdx.x; i < total; i += blockDim.x) {
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
     const int64_t tile = (static_cast<int64_t>(blk) * a.num_kv_heads + h) * G::kTileBytes;
     const u32x4 kv = load16(a.key + src);
     const u32x4 vv = load16(a.value + src);
-    store16(a.k_pool + tile + (q >> 2) * (kBlockSize * 64) + slot * 64 + (q & 3) * 16, kv);
+    store16(a.k_pool + tile + (q >> 2) * G::kChunkRowBytes + slot * 64 + (q & 3) * 16, kv);
     store16(a.v_pool + tile + slot * G::kRowBytes + q * 16, vv);
   }
 }
@@ -57,23 +57,32 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, int chunks
   }
 }
 
-template <DType dt, int D>
+template <DType dt, int D, int B>
 static hipError_t launch_rc(const CacheWriteArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((reshape_and_cache_kernel<dt, D>), dim3(a.num_tokens), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL((reshape_and_cache_kernel<dt, D, B>), dim3(a.num_tokens), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache(DType dt, int head_dim, const CacheWriteArgs& a,
-                                    hipStream_t stream) {
+template <DType dt, int D>
+static hipError_t launch_rc_b(int block_size, const CacheWriteArgs& a, hipStream_t stream) {
+  switch (block_size) {
+    case 8: return launch_rc<dt, D, 8>(a, stream);
+    case 32: return launch_rc<dt, D, 32>(a, stream);
+    default: return launch_rc<dt, D, 16>(a, stream);
+  }
+}
+
+hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
+                                    const CacheWriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   switch (dt) {
-    case DType::F32: return head_dim == 64 ? launch_rc<DType::F32, 64>(a, stream)
-                                           : launch_rc<DType::F32, 128>(a, stream);
-    case DType::F16: return head_dim == 64 ? launch_rc<DType::F16, 64>(a, stream)
-                                           : launch_rc<DType::F16, 128>(a, stream);
-    case DType::BF16: return head_dim == 64 ? launch_rc<DType::BF16, 64>(a, stream)
-                                            : launch_rc<DType::BF16, 128>(a, stream);
+    case DType::F32: return head_dim == 64 ? launch_rc_b<DType::F32, 64>(block_size, a, stream)
+                                           : launch_rc_b<DType::F32, 128>(block_size, a, stream);
+    case DType::F16: return head_dim == 64 ? launch_rc_b<DType::F16, 64>(block_size, a, stream)
+                                           : launch_rc_b<DType::F16, 128>(block_size, a, stream);
+    case DType::BF16: return head_dim == 64 ? launch_rc_b<DType::BF16, 64>(block_size, a, stream)
+                                            : launch_rc_b<DType::BF16, 128>(block_size, a, stream);
   }
   return hipErrorInvalidValue;
 }

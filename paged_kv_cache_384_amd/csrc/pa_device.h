@@ -21,19 +21,22 @@ template <> struct Elem<DType::F32> { static constexpr int kSize = 4; };
 template <> struct Elem<DType::F16> { static constexpr int kSize = 2; };
 template <> struct Elem<DType::BF16> { static constexpr int kSize = 2; };
 
-// Geometry of a (block, head) tile for element type dt and head dimension D, at B = 16.
-template <DType dt, int D>
+// Geometry of a (block, head) tile for element type dt, head dimension D and block size B, and
+// of the 16-token groups the kernels work in. Key tiles are cut into chunk rows of 64 bytes per
+// token (B * 64 bytes per row); value tiles are token rows of D * esz bytes.
+template <DType dt, int D, int B = 16>
 struct TileGeom {
   static constexpr int kEsz = Elem<dt>::kSize;
   static constexpr int kRowBytes = D * kEsz;             // one token's head vector
-  static constexpr int kTileBytes = kBlockSize * kRowBytes;
+  static constexpr int kTileBytes = B * kRowBytes;
+  static constexpr int kChunkRowBytes = B * 64;          // one key chunk row
   static constexpr int kEpp = 16 / kEsz;                 // elements per 16-byte piece
-  static constexpr int kLoads = kTileBytes / 1024;       // 16-byte loads per lane per tile
+  static constexpr int kLoads = kRowBytes / 64;          // 16-byte loads per lane per group
   static constexpr int kChunkElems = 64 / kEsz;          // key layout: elements per chunk
   static constexpr int kPiecesPerRow = kRowBytes / 16;   // value rows: lanes sharing a token
   static constexpr int kRowsPerLoad = 64 / kPiecesPerRow;  // value rows one load covers
-  static_assert(kTileBytes % 1024 == 0, "tile must be whole 1 KiB rows");
-  static_assert(kLoads * kRowsPerLoad == kBlockSize, "value rows must cover the block");
+  static_assert(kRowBytes % 64 == 0, "token rows must be whole 64-byte chunks");
+  static_assert(kLoads * kRowsPerLoad == kGroupTokens, "value rows must cover the group");
 };
 
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {

@@ -8,9 +8,8 @@ namespace pa {
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
-constexpr int kBlockSize = 16;         // token slots per KV block
+constexpr int kGroupTokens = 16;       // tokens one wave-wide key load covers (a 16-token group)
 constexpr int kMaxPartitionTokens = 2048;
-constexpr int kMaxPartitionBlocks = kMaxPartitionTokens / kBlockSize;
 constexpr int kDecodeThreads = 256;    // four 64-lane wavefronts per attention workgroup
 constexpr int kReduceThreads = 256;    // threads of a partition-merge workgroup
 
@@ -67,11 +66,15 @@ struct DecodeArgs {
 };
 
 // Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).
-hipError_t launch_reshape_and_cache(DType dt, int head_dim, const CacheWriteArgs& a,
-                                    hipStream_t stream);
+hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
+                                    const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
-hipError_t launch_decode_attention(DType dt, int head_dim, const DecodeArgs& a,
-                                   hipStream_t stream);
+hipError_t launch_decode_attention_b8(DType dt, int head_dim, const DecodeArgs& a,
+                                      hipStream_t stream);
+hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs& a,
+                                       hipStream_t stream);
+hipError_t launch_decode_attention_b32(DType dt, int head_dim, const DecodeArgs& a,
+                                       hipStream_t stream);
 hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -76,7 +76,10 @@ def test_decode_validation(L):
     assert decode(L, False) == NULL
     assert decode(L, desc(dtype=7)) == UNSUP
     assert decode(L, desc(d=96)) == UNSUP
-    assert decode(L, desc(b=8)) == UNSUP
+    assert decode(L, desc(b=4)) == UNSUP
+    assert decode(L, desc(b=64)) == UNSUP
+    assert decode(L, desc(b=32), part=16) == SHAPE       # partitions are whole blocks
+    assert decode(L, desc(b=8), part=8) == SHAPE         # and whole 16-token groups
     assert decode(L, desc(flags=2)) == UNSUP              # unknown flag bit
     assert decode(L, desc(flags=0x80000000)) == UNSUP
     assert decode(L, desc(nb=0)) == SHAPE
@@ -129,6 +132,12 @@ def test_contiguous_twin_validation(L):
 
 
 def test_workspace_bytes(L):
+    # block sizes 8 and 32: the default partition rounds a short context up to whole
+    # 16-token groups and whole blocks
+    for b, ctx, parts in ((8, 100, 1), (32, 100, 1), (32, 4096, 8)):
+        n = L.pa_decode_workspace_bytes(ctypes.byref(desc(dtype=2, hkv=8, d=128, b=b)), 4, 32,
+                                        ctx, 0)
+        assert n == (0 if parts == 1 else 4 * 32 * parts * 130 * 4), (b, ctx)
     d = desc(dtype=2, hkv=8, d=128)
     # longest context fits the default partition: no workspace
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 512, 0) == 0

@@ -98,3 +98,57 @@ def test_contiguous_twin(name, over):
     for part in (0, 64):
         log(f"[parity] contiguous twin {name} partition={part}")
         run_step(cfg, partition_size=part, twin=True)
+
+
+BLOCK_SHAPES = [(b, dt, d, hq, hkv) for b in (8, 32)
+                for dt, d, hq, hkv in (("f16", 128, 4, 4), ("bf16", 128, 16, 4), ("bf16", 128, 8, 8),
+                                       ("f16", 128, 8, 2), ("f32", 64, 4, 2), ("f16", 64, 6, 2),
+                                       ("f32", 128, 2, 2))]
+
+
+@pytest.mark.parametrize("b,dt,d,hq,hkv", BLOCK_SHAPES,
+                         ids=[f"B{b}-{t}-d{d}-{q}q{k}kv" for b, t, d, q, k in BLOCK_SHAPES])
+def test_block_sizes(b, dt, d, hq, hkv):
+    """Blocks of 8 and 32 tokens: a 16-token group spans two 8-token blocks (lanes 0-31 and
+    32-63 read different physical blocks) or half of a 32-token block."""
+    cfg = wl.DecodeConfig(f"b{b}_{dt}_{d}_{hq}_{hkv}", dt, num_seqs=3, num_q_heads=hq,
+                          num_kv_heads=hkv, head_dim=d, block_size=b, ctx=("uniform", 1, 300),
+                          seed=41)
+    for part in (0, 64):
+        log(f"[parity] block size {b} {dt} d={d} {hq}/{hkv} partition={part}")
+        run_step(cfg, partition_size=part)
+
+
+BLOCK_LENS = {8: (0, 1, 7, 8, 9, 15, 16, 17, 23, 511, 512, 513),
+              32: (0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1025)}
+
+
+@pytest.mark.parametrize("b", [8, 32])
+def test_block_size_boundaries(b):
+    """Contexts ending on either side of block, group and partition boundaries."""
+    lens = BLOCK_LENS[b]
+    for dt in ("bf16", "f16"):
+        cfg = wl.DecodeConfig(f"b{b}_bounds_{dt}", dt, num_seqs=len(lens), num_q_heads=8,
+                              num_kv_heads=2, head_dim=128, block_size=b, ctx=("fixed", lens),
+                              seed=43)
+        for part in (0, max(16, b), 512):
+            log(f"[parity] block size {b} boundaries {dt} partition={part}")
+            run_step(cfg, partition_size=part)
+
+
+@pytest.mark.parametrize("b", [8, 32])
+def test_block_size_cow_and_twin(b):
+    """Copy-on-write of a shared partial block and the contiguous twin at block sizes 8, 32."""
+    cow = wl.DecodeConfig(f"b{b}_cow", "f16", num_seqs=8, num_q_heads=4, num_kv_heads=4,
+                          head_dim=128, block_size=b, ctx=("shared_prefix", 44, 1, 70, 4),
+                          seed=47)
+    assert wl.build_batch(cow).copy_pairs.shape[0] > 0
+    for shared in (True, False):
+        log(f"[parity] block size {b} copy-on-write shared_blocks={shared}")
+        run_step(cow, partition_size=0, shared_blocks=shared)
+    twin = wl.DecodeConfig(f"b{b}_twin", "bf16", num_seqs=5, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, block_size=b, ctx=("uniform", 1, 700),
+                           placement="contiguous", seed=53)
+    for part in (0, 64):
+        log(f"[parity] block size {b} contiguous twin partition={part}")
+        run_step(twin, partition_size=part, twin=True)
