@@ -154,6 +154,48 @@ def paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream):
     return res
 
 
+def swap_rate(cfg, batch, v, stream, reps=5):
+    """Every block of the first half of the sequences swapped out to a pinned host pool and back
+    into the same GPU blocks (pa_swap_blocks, copy engines over the host link), HIP events on
+    the stream; GB/s counts key and value bytes once per direction."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_384_amd as pa
+    B = cfg.block_size
+    rows = []
+    for s_ in range(cfg.num_seqs // 2):
+        nb = -(-int(batch.context_lens[s_]) // B)
+        rows.extend(batch.block_tables[s_, :nb].tolist())
+    gpu_ids = np.array(rows, np.int32)
+    n = len(gpu_ids)
+    host_shape = (n,) + tuple(v["k_pool"].shape[1:])
+    hk = torch.empty(host_shape, dtype=v["k_pool"].dtype, pin_memory=True)
+    hv = torch.empty(host_shape, dtype=v["k_pool"].dtype, pin_memory=True)
+    out_pairs = np.stack([gpu_ids, np.arange(n, dtype=np.int32)], 1)
+    in_pairs = out_pairs[:, ::-1].copy()
+    block_bytes = v["k_pool"][0].numel() * v["k_pool"].element_size()
+    nbytes = 2 * n * block_bytes
+    res = {"blocks": n, "bytes_per_direction": nbytes}
+    for name, args_ in (("out", (hk, hv, v["k_pool"], v["v_pool"], out_pairs)),
+                        ("in", (v["k_pool"], v["v_pool"], hk, hv, in_pairs))):
+        pa.pa_swap_blocks(*args_, head_dim=cfg.head_dim)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            pa.pa_swap_blocks(*args_, head_dim=cfg.head_dim)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        res[f"{name}_us"] = round(us, 1)
+        res[f"{name}_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 2)
+    print(f"[bench] swap {n} blocks ({nbytes / 1e6:.1f} MB each way): out {res['out_gbps']} GB/s, "
+          f"in {res['in_gbps']} GB/s", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +215,9 @@ def main():
     ap.add_argument("--paging-overhead", action="store_true",
                     help="also time pa_decode against its contiguous twin (no block table) on a "
                          "contiguously laid out copy of the batch")
+    ap.add_argument("--swap", action="store_true",
+                    help="also time swapping every block of half the sequences out to pinned "
+                         "host memory and back (pa_swap_blocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -305,6 +350,10 @@ def main():
                 "kernel": "decode_attention_kernel", "avg_us": round(attn_avg, 2),
                 "bytes_per_launch": kv_bytes}
 
+    swap = None
+    if args.swap:
+        swap = swap_rate(cfg, batch, sets[0], stream)
+
     paging = None
     if args.paging_overhead:
         paging = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream)
@@ -347,6 +396,8 @@ def main():
     }
     if paging is not None:
         line["paging_overhead"] = paging
+    if swap is not None:
+        line["swap"] = swap
     print(json.dumps(line), flush=True)
 
 

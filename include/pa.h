@@ -3,7 +3,7 @@
  *
  * Plain C ABI: raw pointers and sizes, no HIP or PyTorch types. Streams are hipStream_t
  * handles passed as void* (NULL = the default stream). All device buffers are owned by the
- * caller; the library allocates nothing and keeps no per-call state. Every call is
+ * caller; the library allocates no device memory and keeps no per-call state. Every call is
  * asynchronous on its stream.
  *
  * Sources, cited by page title and section:
@@ -53,6 +53,13 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+/* The library exports these functions and nothing else. */
+#if defined(__GNUC__) || defined(__clang__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
 #endif
 
 #define PA_ABI_VERSION 2
@@ -112,7 +119,7 @@ typedef struct {
  * is at or past max_blocks_per_seq * B is skipped; a block id outside [0, NB) is clamped into
  * range (no fault, but the write lands in the wrong block).
  */
-pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* value_cache,
+PA_API pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* value_cache,
                                const void* key, const void* value, const int32_t* block_tables,
                                int32_t num_seqs, int32_t max_blocks_per_seq,
                                const int32_t* token_seq, const int32_t* token_pos,
@@ -123,7 +130,7 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* va
  * partition_size 0 means the library's choice (the same one pa_decode makes). Returns 0 when
  * no workspace is needed (every context fits one partition) and (size_t)-1 for invalid sizes.
  */
-size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t partition_size);
 
 /*
@@ -157,7 +164,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32
  * WORKSPACE); a failed launch gives PA_ERR_LAUNCH. num_seqs = 0 returns PA_OK. A block id
  * outside [0, NB) is clamped into range (no fault, but the result is then meaningless).
  */
-pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
+PA_API pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
                     void* out, const void* query, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, float scale, int32_t max_context_len,
@@ -171,13 +178,13 @@ pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* v
  * otherwise); pa_decode_reduce merges the partition states into out. pa_decode_reduce launches
  * nothing when every context fits one partition.
  */
-pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,
+PA_API pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,
                               const void* value_cache, void* out, const void* query,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                               float scale, int32_t max_context_len, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, void* stream);
-pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
+PA_API pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
                            const void* value_cache, void* out, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -196,7 +203,7 @@ pa_status pa_decode_reduce(const pa_cache_desc* c, const void* key_cache,
  * key/value tiles are always streamed; PA_CACHE_SHARED_BLOCKS gives PA_ERR_UNSUPPORTED.
  * num_seqs * max_blocks_per_seq > num_blocks gives PA_ERR_SHAPE.
  */
-pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
+PA_API pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
                                const void* value_cache, void* out, const void* query,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_q_heads, float scale,
@@ -215,14 +222,39 @@ pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
  * Caller contract: destination ids are distinct and none is also a source in the same call
  * (otherwise the copies race). A pair with an id outside [0, NB) is skipped.
  */
-pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,
+PA_API pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,
+                         const int32_t* src_dst, int32_t num_pairs, void* stream);
+
+/*
+ * pa_swap_blocks — copy whole blocks between two pools of the same shape, one of which may live
+ * in host memory: the swap of a preempted sequence's blocks out to CPU memory and back
+ * ([anal] §6: the evicted blocks move to a CPU block pool, bounded by the GPU's block count).
+ *
+ * For each pair k: block src_dst[2k] of the source pools (src_key, src_value) is copied to block
+ * src_dst[2k+1] of the destination pools (dst_key, dst_value): every KV head and every slot, bit
+ * for bit, by one kernel that reads or writes the host pool across the host link.
+ *
+ *   dst, src        descriptors of the two pool pairs: same dtype, num_kv_heads, head_dim and
+ *                   block_size (else PA_ERR_SHAPE); num_blocks may differ
+ *   dst_*, src_*    device memory or pinned host memory (hipHostMalloc), in the layout above;
+ *                   each pointer is resolved on the host (hipPointerGetAttributes) to the
+ *                   address the device uses, and memory the device cannot address (pageable
+ *                   host memory) gives PA_ERR_UNSUPPORTED before anything is launched
+ *   src_dst         int32 [num_pairs][2], device or pinned host memory; a pair with an id
+ *                   outside its pool is skipped
+ *   num_pairs = 0   returns PA_OK without launching
+ * Caller contract: destination ids distinct, and a swap within one pool pair must not overlap a
+ * source with a destination (the copies would race).
+ */
+PA_API pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_value,
+                         const pa_cache_desc* src, const void* src_key, const void* src_value,
                          const int32_t* src_dst, int32_t num_pairs, void* stream);
 
 /* Static description of a status code (never NULL). */
-const char* pa_status_string(pa_status s);
+PA_API const char* pa_status_string(pa_status s);
 
 /* PA_ABI_VERSION of the built library. */
-int32_t pa_abi_version(void);
+PA_API int32_t pa_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ from .paged_attention import (  # noqa: F401
     reshape_and_cache_ref,
     slot_of,
     storage_dtype,
+    swap_blocks_ref,
     to_f64,
     token_kv,
     v_offset,

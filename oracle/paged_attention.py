@@ -300,3 +300,24 @@ def copy_blocks_ref(k_pool, v_pool, pairs, *, dtype, num_kv_heads, block_size, h
         kf[k_offset(dst, h, t, i, esz=esz, **kw)] = kf[k_offset(src, h, t, i, esz=esz, **kw)]
         vf[v_offset(dst, h, t, i, **kw)] = vf[v_offset(src, h, t, i, **kw)]
     return k_out, v_out
+
+
+def swap_blocks_ref(dst_k, dst_v, src_k, src_v, pairs, *, dtype, num_kv_heads, block_size,
+                    head_dim):
+    """Copies of the destination pools where, for each (src, dst) pair, destination block dst
+    receives all of source block src's key and value elements (every KV head, every slot), bit
+    for bit ([anal] §6: a preempted sequence's blocks are swapped out to a CPU block pool and
+    back in, block by block)."""
+    esz = _ESZ[dtype]
+    k_out = np.array(dst_k, copy=True)
+    v_out = np.array(dst_v, copy=True)
+    kf, vf = _flat(k_out), _flat(v_out)
+    ksf, vsf = _flat(np.asarray(src_k)), _flat(np.asarray(src_v))
+    h = np.arange(num_kv_heads)[:, None, None]
+    t = np.arange(block_size)[None, :, None]
+    i = np.arange(head_dim)[None, None, :]
+    kw = dict(num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        kf[k_offset(dst, h, t, i, esz=esz, **kw)] = ksf[k_offset(src, h, t, i, esz=esz, **kw)]
+        vf[v_offset(dst, h, t, i, **kw)] = vsf[v_offset(src, h, t, i, **kw)]
+    return k_out, v_out

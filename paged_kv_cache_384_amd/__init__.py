@@ -21,7 +21,7 @@ import os
 
 __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
-    "pa_decode_reduce", "pa_decode_contiguous", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
+    "pa_decode_reduce", "pa_decode_contiguous", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +33,7 @@ library_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
-                    "pa_copy_blocks", "pa_status_string", "pa_abi_version"]
+                    "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_contiguous.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                            ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t, _vp]
         L.pa_decode_contiguous.restype = ctypes.c_int
+        L.pa_swap_blocks.argtypes = [_desc_p, _vp, _vp, _desc_p, _vp, _vp, _vp, _i32, _vp]
+        L.pa_swap_blocks.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_desc_p, _vp, _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -279,3 +281,34 @@ def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size
             _dev(src_dst, "src_dst", torch.int32), pairs.shape[0] if src_dst.numel() else 0,
             _stream(key_cache, stream))
     _check(lib().pa_copy_blocks(*args), "pa_copy_blocks")
+
+
+def pa_swap_blocks(dst_key, dst_value, src_key, src_value, src_dst, *, head_dim: int,
+                   block_size: int | None = None, stream=None) -> None:
+    """Copy block src_dst[k, 0] of the source pools onto block src_dst[k, 1] of the destination
+    pools. Pools are GPU tensors or pinned CPU tensors (``pin_memory=True``) of the same shape
+    apart from the number of blocks; ``src_dst`` holds int32 pairs (a GPU tensor, or any array,
+    which is then copied to the GPU)."""
+    import numpy as np
+    import torch
+
+    def ptr(t, what):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous torch tensor")
+        if t.device.type != "cuda" and not t.is_pinned():
+            raise ValueError(f"{what} must be on the GPU or in pinned host memory")
+        return _vp(t.data_ptr())
+
+    dd = _desc(dst_key, head_dim, block_size)
+    sd = _desc(src_key, head_dim, block_size)
+    if dst_value.shape != dst_key.shape or src_value.shape != src_key.shape:
+        raise ValueError("key and value pools differ in shape")
+    gpu = dst_key if dst_key.device.type == "cuda" else src_key
+    if not (isinstance(src_dst, torch.Tensor) and src_dst.device.type == "cuda"):
+        src_dst = torch.as_tensor(np.ascontiguousarray(src_dst, dtype=np.int32)).to(gpu.device)
+    if src_dst.dtype != torch.int32 or src_dst.numel() % 2 or not src_dst.is_contiguous():
+        raise ValueError("src_dst must hold contiguous int32 (src, dst) pairs")
+    args = (ctypes.byref(dd), ptr(dst_key, "dst_key"), ptr(dst_value, "dst_value"),
+            ctypes.byref(sd), ptr(src_key, "src_key"), ptr(src_value, "src_value"),
+            _vp(src_dst.data_ptr()), src_dst.numel() // 2, _stream(gpu, stream))
+    _check(lib().pa_swap_blocks(*args), "pa_swap_blocks")

@@ -17,7 +17,7 @@ SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_attention_b8.hip", "pa_attention_b1
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32 (plain fp32 VALU only).
 # The host pass warns that it does not know the feature; that is expected.
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
 

@@ -1,6 +1,6 @@
 // C ABI of the paged decode library: argument checks on the host, partition choice, dispatch.
-// Every check runs before any HIP call; the only HIP calls are the launches and
-// hipGetLastError. Nothing is allocated.
+// Every check runs before any launch; besides the launches and hipGetLastError the only HIP call
+// is pa_swap_blocks' pointer query (hipPointerGetAttributes). No device memory is allocated.
 #include <stdint.h>
 
 #include "../../include/pa.h"
@@ -156,6 +156,21 @@ pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void
   return PA_OK;
 }
 
+// The address a kernel uses for `p`: device memory as it is, pinned host memory through its
+// device mapping; nullptr for memory the device cannot address (ordinary pageable host memory).
+void* device_address(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error the query left for pageable memory
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return const_cast<void*>(p);
+  // pinned host memory: the query reports the address itself as the host address and a device
+  // mapping; anything else is refused rather than guessed
+  if (attr.type != hipMemoryTypeHost || attr.hostPointer != p) return nullptr;
+  return attr.devicePointer;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,12 +272,45 @@ pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_ca
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(src_dst, 4))
     return PA_ERR_ALIGN;
   pa::CopyArgs a;
-  a.k_pool = static_cast<uint8_t*>(key_cache);
-  a.v_pool = static_cast<uint8_t*>(value_cache);
+  a.src_k = a.dst_k = static_cast<uint8_t*>(key_cache);
+  a.src_v = a.dst_v = static_cast<uint8_t*>(value_cache);
   a.pairs = src_dst;
   a.num_pairs = num_pairs;
-  a.num_blocks = c->num_blocks;
+  a.src_num_blocks = a.dst_num_blocks = c->num_blocks;
   a.block_bytes = tile_bytes(c) * c->num_kv_heads;
+  const int64_t chunks = (a.block_bytes / 16 + 2047) / 2048;
+  if (chunks * num_pairs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_value,
+                         const pa_cache_desc* src, const void* src_key, const void* src_value,
+                         const int32_t* src_dst, int32_t num_pairs, void* stream) {
+  pa_status st = check_desc(dst);
+  if (st != PA_OK) return st;
+  if ((st = check_desc(src)) != PA_OK) return st;
+  if (dst->dtype != src->dtype || dst->num_kv_heads != src->num_kv_heads ||
+      dst->head_dim != src->head_dim || dst->block_size != src->block_size)
+    return PA_ERR_SHAPE;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_key || !dst_value || !src_key || !src_value || !src_dst) return PA_ERR_NULL;
+  if (!aligned(dst_key, 16) || !aligned(dst_value, 16) || !aligned(src_key, 16) ||
+      !aligned(src_value, 16) || !aligned(src_dst, 4))
+    return PA_ERR_ALIGN;
+  pa::CopyArgs a;
+  a.dst_k = static_cast<uint8_t*>(device_address(dst_key));
+  a.dst_v = static_cast<uint8_t*>(device_address(dst_value));
+  a.src_k = static_cast<const uint8_t*>(device_address(src_key));
+  a.src_v = static_cast<const uint8_t*>(device_address(src_value));
+  a.pairs = static_cast<const int32_t*>(device_address(src_dst));
+  if (!a.dst_k || !a.dst_v || !a.src_k || !a.src_v || !a.pairs) return PA_ERR_UNSUPPORTED;
+  a.num_pairs = num_pairs;
+  a.src_num_blocks = src->num_blocks;
+  a.dst_num_blocks = dst->num_blocks;
+  a.block_bytes = tile_bytes(src) * src->num_kv_heads;
   const int64_t chunks = (a.block_bytes / 16 + 2047) / 2048;
   if (chunks * num_pairs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
   if (pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) != hipSuccess)

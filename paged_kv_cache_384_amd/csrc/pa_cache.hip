@@ -38,22 +38,25 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   }
 }
 
-// Grid: num_pairs * chunks workgroups; each copies its chunk of one block in both pools.
+// Grid: num_pairs * chunks workgroups; each copies its chunk of one block in both pools. A
+// pair with an id outside its pool is skipped. One of the pools may be pinned host memory (a
+// swap): the loads or stores then cross the host link, 16 bytes per lane, a whole wave's 1 KiB
+// contiguous.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, int chunks,
                                                           int64_t chunk_pieces) {
   const int pair = blockIdx.x / chunks;
   const int chunk = blockIdx.x % chunks;
   const int src = a.pairs[2 * pair];
   const int dst = a.pairs[2 * pair + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  if (src < 0 || src >= a.src_num_blocks || dst < 0 || dst >= a.dst_num_blocks) return;
   const int64_t pieces = a.block_bytes / 16;
   const int64_t p0 = chunk * chunk_pieces;
   const int64_t p1 = p0 + chunk_pieces < pieces ? p0 + chunk_pieces : pieces;
   const int64_t so = static_cast<int64_t>(src) * a.block_bytes;
   const int64_t d0 = static_cast<int64_t>(dst) * a.block_bytes;
   for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-    store16(a.k_pool + d0 + p * 16, load16(a.k_pool + so + p * 16));
-    store16(a.v_pool + d0 + p * 16, load16(a.v_pool + so + p * 16));
+    store16(a.dst_k + d0 + p * 16, load16(a.src_k + so + p * 16));
+    store16(a.dst_v + d0 + p * 16, load16(a.src_v + so + p * 16));
   }
 }
 

@@ -28,12 +28,17 @@ struct CacheWriteArgs {
   int32_t num_kv_heads;
 };
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools for copy-on-write
+// copies, a device pool and a pinned host pool (by its device address) for swaps.
 struct CopyArgs {
-  uint8_t* k_pool;
-  uint8_t* v_pool;
-  const int32_t* pairs;
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* dst_k;
+  uint8_t* dst_v;
+  const int32_t* pairs;  // [num_pairs][2] (source block, destination block)
   int32_t num_pairs;
-  int32_t num_blocks;
+  int32_t src_num_blocks;
+  int32_t dst_num_blocks;
   int64_t block_bytes;  // bytes of one physical block in one pool (all KV heads)
 };
 

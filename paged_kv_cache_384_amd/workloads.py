@@ -236,6 +236,39 @@ class BlockManager:
         self.tables[seq] = []
         self.lengths[seq] = 0
 
+    def swap_out(self, seq: int, cpu: "BlockManager") -> tuple[int, np.ndarray]:
+        """Move a sequence's blocks to the CPU block pool ``cpu`` ([anal] §6: a preempted
+        sequence's blocks are evicted to CPU memory, all of them or none). Every GPU block gets
+        a free CPU block and is released here; the sequence continues in ``cpu`` under the
+        returned id. Returns (cpu sequence id, (gpu block, cpu block) copy pairs). Raises
+        PoolExhausted, changing nothing, when the CPU pool cannot take every block, and
+        ValueError for a sequence with shared blocks (those stay resident)."""
+        t = self.tables[seq]
+        if any(self.ref[b] != 1 for b in t):
+            raise ValueError("a sequence with shared blocks is not swapped out")
+        if cpu.num_free < len(t):
+            raise PoolExhausted("the CPU block pool cannot take the whole sequence")
+        cs = cpu.new_sequence()
+        pairs = [(b, cpu.take()) for b in t]
+        cpu.tables[cs] = [c for _, c in pairs]
+        cpu.lengths[cs] = self.lengths[seq]
+        self.free_sequence(seq)
+        return cs, np.array(pairs, dtype=np.int32).reshape(-1, 2)
+
+    def swap_in(self, cpu: "BlockManager", cpu_seq: int) -> tuple[int, np.ndarray]:
+        """Bring a swapped-out sequence back: fresh GPU blocks for all of its CPU blocks (or
+        PoolExhausted, changing nothing). Returns (gpu sequence id, (cpu block, gpu block)
+        copy pairs); the CPU blocks are released."""
+        t = cpu.tables[cpu_seq]
+        if self.num_free < len(t):
+            raise PoolExhausted("not enough free GPU blocks to swap the sequence in")
+        gs = self.new_sequence()
+        pairs = [(c, self.take()) for c in t]
+        self.tables[gs] = [g for _, g in pairs]
+        self.lengths[gs] = cpu.lengths[cpu_seq]
+        cpu.free_sequence(cpu_seq)
+        return gs, np.array(pairs, dtype=np.int32).reshape(-1, 2)
+
     def wasted_slots(self, seq: int) -> int:
         """Allocated but unfilled token slots of ``seq`` (only its last block can have any)."""
         return len(self.tables[seq]) * self.block_size - self.lengths[seq]

@@ -183,3 +183,42 @@ def test_binding_names_match_c_names():
     for name in pa.EXPORTED_SYMBOLS:
         if name != "pa_decode_workspace_bytes":
             assert callable(getattr(pa, name)), name
+
+
+def test_library_exports_the_abi_and_imports_only_long_standing_hip_symbols():
+    """Only the functions pa.h declares are exported as code (the other dynamic symbols are the
+    kernel handles the HIP runtime registers), and every HIP symbol the library imports carries
+    the hip_4.2 version: the HIP runtime loaded in a process may be an older one than the
+    toolchain that built the library (torch ships its own), so a newer symbol would keep the
+    library from loading."""
+    import shutil
+    import subprocess
+    if not os.path.exists(pa.library_path) or shutil.which("nm") is None:
+        pytest.skip("libpa.so not built or nm missing")
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines()
+                if ln.split() and ln.split()[-2] in ("T", "W")}
+    assert exported == set(header_functions()), sorted(exported ^ set(header_functions()))[:10]
+    out = subprocess.run(["nm", "-D", "--undefined-only", pa.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    hip = [ln.split()[-1] for ln in out.splitlines() if "hip" in ln.lower()]
+    assert hip and all(sym.endswith("@hip_4.2") for sym in hip), hip
+
+
+def test_swap_validation(L):
+    """Both pools of one shape apart from the block count; pointers checked before anything
+    runs (the pointer query that follows needs a GPU, so only failures before it run here)."""
+    def sw(dd, ss, pairs, n, dk=GOOD):
+        return L.pa_swap_blocks(ctypes.byref(dd), dk, GOOD, ctypes.byref(ss), GOOD, GOOD,
+                                pairs, n, P(0))
+    assert sw(desc(), desc(d=64), GOOD, 2) == SHAPE            # head_dim differs
+    assert sw(desc(), desc(b=32), GOOD, 2) == SHAPE            # block size differs
+    assert sw(desc(), desc(dtype=2), GOOD, 2) == SHAPE         # dtype differs
+    assert sw(desc(), desc(flags=8), GOOD, 2) == UNSUP
+    assert sw(desc(), desc(), P(0), 2) == NULL
+    assert sw(desc(), desc(), GOOD, 2, dk=P(0)) == NULL
+    assert sw(desc(), desc(), GOOD, -1) == SHAPE
+    assert sw(desc(), desc(), GOOD, 2, dk=ODD) == ALIGN
+    assert sw(desc(), desc(), P(0x10002), 2) == ALIGN
+    assert sw(desc(), desc(), P(0), 0) == OK

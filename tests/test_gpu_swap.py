@@ -1,0 +1,78 @@
+"""Block swap between the GPU pools and pinned host pools ([anal] §6: a preempted sequence's
+blocks move to a CPU block pool and back), through the C ABI: both pools are compared with the
+oracle's copies bit for bit, and decoding through the remapped table after the round trip
+reproduces the output from before it exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_384_amd as pa
+from paged_kv_cache_384_amd import workloads as wl
+from _gpu_cases import log
+from _helpers import from_storage, random_storage, to_storage
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt,b", [("bf16", 16), ("f16", 8), ("f32", 32), ("bf16", 32)])
+def test_swap_round_trip(dt, b):
+    dev = torch.device("cuda:0")
+    d = 64 if dt == "f32" else 128
+    cfg = wl.DecodeConfig(f"swap_{dt}_{b}", dt, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                          head_dim=d, block_size=b, ctx=("fixed", (50, 300, 17, 129)),
+                          num_blocks=120, seed=61)
+    batch = wl.build_batch(cfg)
+    vals = wl.make_values(batch, device="cpu", poison_nan=False)
+    kp, vp, q = to_storage(vals["k_pool"]), to_storage(vals["v_pool"]), to_storage(vals["query"])
+    kw = dict(dtype=dt, num_kv_heads=2, block_size=b, head_dim=d)
+    gk, gv = from_storage(kp, dt).to(dev), from_storage(vp, dt).to(dev)
+    q_d = from_storage(q, dt).to(dev)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    ctx = torch.from_numpy(batch.context_lens).to(dev)
+    out0 = torch.empty_like(q_d)
+    pa.pa_decode(out0, q_d, gk, gv, bt, ctx, cfg.scale, batch.max_context_len)
+
+    # host pools hold random bits, so a stray write shows
+    rng = np.random.default_rng(5)
+    nb_host = 40
+    hk_np = random_storage(rng, (nb_host,) + kp.shape[1:], dt)
+    hv_np = random_storage(rng, (nb_host,) + kp.shape[1:], dt)
+    hk = from_storage(hk_np, dt).pin_memory()
+    hv = from_storage(hv_np, dt).pin_memory()
+    s = 1
+    nb = -(-int(batch.context_lens[s]) // b)
+    row = batch.block_tables[s, :nb]
+    host_ids = rng.permutation(nb_host)[:nb].astype(np.int32)
+    out_pairs = np.stack([row, host_ids], 1)
+    log(f"[swap] {dt} B={b}: {nb} blocks out to pinned host memory")
+    pa.pa_swap_blocks(hk, hv, gk, gv, out_pairs, head_dim=d)
+    torch.cuda.synchronize()
+    ek, ev = oracle.swap_blocks_ref(hk_np, hv_np, kp, vp, out_pairs, **kw)
+    assert np.array_equal(to_storage(hk), ek) and np.array_equal(to_storage(hv), ev)
+
+    # the GPU blocks are reused meanwhile; the sequence comes back into fresh blocks
+    gk[torch.from_numpy(row).long()] = from_storage(random_storage(rng, (nb,) + kp.shape[1:], dt),
+                                                    dt).to(dev)
+    used = set(batch.block_tables.ravel().tolist())
+    fresh = np.array([x for x in rng.permutation(batch.num_blocks) if x not in used][:nb],
+                     np.int32)
+    in_pairs = np.stack([host_ids, fresh], 1)
+    log(f"[swap] {dt} B={b}: back into fresh GPU blocks")
+    before = to_storage(gk)
+    pa.pa_swap_blocks(gk, gv, hk, hv, in_pairs, head_dim=d)
+    torch.cuda.synchronize()
+    ek2, ev2 = oracle.swap_blocks_ref(before, to_storage(gv), ek, ev, in_pairs, **kw)
+    assert np.array_equal(to_storage(gk), ek2) and np.array_equal(to_storage(gv), ev2)
+
+    tables = batch.block_tables.copy()
+    tables[s, :nb] = fresh
+    out1 = torch.full_like(q_d, float("nan"))
+    pa.pa_decode(out1, q_d, gk, gv, torch.from_numpy(tables).to(dev), ctx, cfg.scale,
+                 batch.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_storage(out1), to_storage(out0))
+    ref = oracle.paged_decode_ref(q, to_storage(gk), to_storage(gv), tables, batch.context_lens,
+                                  cfg.scale, **kw)
+    tol = 1e-5 if dt == "f32" else 1e-2
+    assert float(np.abs(oracle.to_f64(to_storage(out1), dt) - ref).max()) <= tol

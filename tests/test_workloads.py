@@ -195,3 +195,67 @@ def test_shares_blocks_flags_only_the_shared_prefix_workload():
     assert wl.build_batch(wl.CONFIGS["cow_fp16"]).shares_blocks
     for name in ("tiny_fp32", "opt13b_fp16", "gqa_bf16", "long_bf16"):
         assert not wl.build_batch(wl.CONFIGS[name]).shares_blocks
+
+
+def test_swap_out_and_in_move_whole_sequences():
+    """[anal] §6: a preempted sequence's blocks go to a CPU pool, all or none, and come back to
+    fresh GPU blocks; shared blocks are not swapped."""
+    rng = np.random.default_rng(5)
+    gpu = wl.BlockManager(40, 16, rng=rng)
+    cpu = wl.BlockManager(8, 16, rng=rng)
+    a, b = gpu.new_sequence(), gpu.new_sequence()
+    gpu.append_tokens(a, 100)          # 7 blocks
+    gpu.append_tokens(b, 200)          # 13 blocks
+    free0 = gpu.num_free
+    blocks_a = list(gpu.tables[a])
+    cs, out_pairs = gpu.swap_out(a, cpu)
+    assert out_pairs.shape == (7, 2) and list(out_pairs[:, 0]) == blocks_a
+    assert gpu.num_free == free0 + 7 and cpu.num_free == 1
+    assert cpu.lengths[cs] == 100 and len(set(out_pairs[:, 1])) == 7
+    assert all(cpu.ref[c] == 1 for c in out_pairs[:, 1]) and all(gpu.ref[g] == 0 for g in blocks_a)
+    # all or nothing: b needs 13 CPU blocks, 1 is free
+    with pytest.raises(wl.PoolExhausted):
+        gpu.swap_out(b, cpu)
+    assert len(gpu.tables[b]) == 13 and cpu.num_free == 1
+    gs, in_pairs = gpu.swap_in(cpu, cs)
+    assert list(in_pairs[:, 0]) == list(out_pairs[:, 1])
+    assert gpu.tables[gs] == list(in_pairs[:, 1]) and gpu.lengths[gs] == 100
+    assert cpu.num_free == 8 and gpu.num_free == free0
+    # shared blocks stay resident
+    c = gpu.fork(b)
+    with pytest.raises(ValueError):
+        gpu.swap_out(c, cpu)
+
+
+def test_swap_round_trip_through_the_oracle_reproduces_attention():
+    """Blocks copied GPU -> CPU -> fresh GPU blocks (oracle copies) give the same attention
+    output, bit for bit, through the remapped table."""
+    import oracle
+    cfg = wl.DecodeConfig("swap", "bf16", num_seqs=3, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                          ctx=("fixed", (37, 80, 5)), num_blocks=40, seed=9)
+    batch = wl.build_batch(cfg)
+    vals = wl.make_values(batch, device="cpu", poison_nan=False)
+    from _helpers import to_storage
+    kp, vp, q = to_storage(vals["k_pool"]), to_storage(vals["v_pool"]), to_storage(vals["query"])
+    kw = dict(dtype="bf16", num_kv_heads=2, block_size=16, head_dim=64)
+    ref = oracle.paged_decode_ref(q, kp, vp, batch.block_tables, batch.context_lens, cfg.scale,
+                                  **kw)
+    # host pools of 10 blocks; sequence 1 (5 blocks) goes out and comes back elsewhere
+    ck = np.zeros((10,) + kp.shape[1:], kp.dtype)
+    cv = np.zeros_like(ck)
+    row = batch.block_tables[1, :5]
+    out_pairs = np.stack([row, np.arange(5)], 1)
+    ck, cv = oracle.swap_blocks_ref(ck, cv, kp, vp, out_pairs, **kw)
+    kp2 = np.full_like(kp, 0x7fc0)  # the GPU blocks are reused meanwhile
+    vp2 = np.full_like(vp, 0x7fc0)
+    for s in (0, 2):
+        nb = -(-int(batch.context_lens[s]) // 16)
+        blk = batch.block_tables[s, :nb]
+        kp2[blk], vp2[blk] = kp[blk], vp[blk]
+    used = set(batch.block_tables.ravel().tolist())  # includes the poison block
+    fresh = np.array([b for b in range(batch.num_blocks) if b not in used][:5], np.int32)
+    kp2, vp2 = oracle.swap_blocks_ref(kp2, vp2, ck, cv, np.stack([np.arange(5), fresh], 1), **kw)
+    tables = batch.block_tables.copy()
+    tables[1, :5] = fresh
+    got = oracle.paged_decode_ref(q, kp2, vp2, tables, batch.context_lens, cfg.scale, **kw)
+    assert np.array_equal(got, ref)
