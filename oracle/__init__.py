@@ -11,6 +11,7 @@ from .paged_attention import (  # noqa: F401
     k_offset,
     merge_partition_states_ref,
     paged_decode_ref,
+    paged_prefill_ref,
     partition_states_ref,
     reshape_and_cache_ref,
     slot_of,

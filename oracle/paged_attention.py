@@ -1,4 +1,4 @@
-"""CPU oracle for the paged KV-cache decode path.
+"""CPU oracle for the paged KV-cache attention path (decode, prefill, cache writes, block copies).
 
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
 of ``bench.py`` may import this module. It shares no code with the HIP library (no kernels,
@@ -35,6 +35,10 @@ Readings where the pages leave a step open (each is listed with its reason in th
   * The scale is the caller's float32 ``scale`` (1/sqrt(d) in every workload), widened exactly.
   * Grouped-query attention (not on the pages): query head h reads KV head h // (Hq / Hkv).
   * ctx = 0 gives a zero output.
+  * Prefill (several query tokens of one sequence at once): the q_len queries are the
+    sequence's newest tokens, already written to the cache, so query j sits at position
+    ctx - q_len + j and the dense formula for that position applies unchanged (each query
+    attends to itself and everything before it, nothing after).
 
 The physical pool layout is the library's choice, fixed by its header; ``k_offset`` and
 ``v_offset`` below restate it from that description and are pinned by layout properties in
@@ -172,6 +176,45 @@ def paged_decode_ref(query, k_pool, v_pool, block_tables, context_lens, scale, *
         for m, h in enumerate(heads):
             g = h // G
             out[n, m] = attention_one_query(q64[s, h], K[:, g, :], V[:, g, :], scale64)
+    return out
+
+
+def paged_prefill_ref(query, k_pool, v_pool, block_tables, query_start, context_lens, scale, *,
+                      dtype, num_kv_heads, block_size, head_dim, seqs=None, rows=None):
+    """Causal attention of every query token over its sequence's paged KV cache ([wiki] dense
+    form for a general query i: token i attends to tokens 1..i; the blocked form sums over the
+    first ceil(i/B) blocks).
+
+    Sequence s's queries are rows query_start[s] .. query_start[s+1]-1 of ``query`` (stored
+    [T, Hq, d]); they are its newest q_len = query_start[s+1] - query_start[s] tokens, so query j
+    sits at position p = ctx - q_len + j (0-based) and attends to tokens 0..p of the cache
+    (q_len = 1 is a decode step, q_len = ctx a whole prompt). ``seqs`` selects sequences,
+    ``rows`` (a dict seq -> list of j) selects queries within them. Returns a dict
+    (s, j) -> float64 [Hq, d].
+    """
+    q64 = to_f64(query, dtype)
+    T, Hq, d = q64.shape
+    G = Hq // num_kv_heads
+    scale64 = float(np.float32(scale))
+    S = len(context_lens)
+    seqs = range(S) if seqs is None else list(seqs)
+    out = {}
+    for s in seqs:
+        ctx = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        q_len = q1 - q0
+        K, V = gather_sequence_kv(k_pool, v_pool, block_tables[s], ctx, dtype=dtype,
+                                  num_kv_heads=num_kv_heads, block_size=block_size,
+                                  head_dim=head_dim)
+        js = range(q_len) if rows is None else rows[s]
+        for j in js:
+            p = ctx - q_len + j
+            o = np.zeros((Hq, d))
+            for h in range(Hq):
+                g = h // G
+                o[h] = attention_one_query(q64[q0 + j, h], K[:p + 1, g, :], V[:p + 1, g, :],
+                                           scale64)
+            out[(s, j)] = o
     return out
 
 

@@ -436,7 +436,109 @@ def pin_split_merge(oracle):
         assert np.abs(oracle.merge_partition_states_ref(states) - whole).max() <= 1e-13
 
 
+# ---------------------------------------------------------------------------------------------
+# prefill: every query token of a prompt (or of a chunk of one) attends causally
+# ---------------------------------------------------------------------------------------------
+
+def _prefill_case(rng, *, q_lens, **kw):
+    """A decode case whose sequences also carry q_lens new query tokens each (their newest)."""
+    c = make_case(rng, **kw)
+    q_lens = np.asarray(q_lens, np.int32)
+    qs = np.zeros(c["S"] + 1, np.int32)
+    qs[1:] = np.cumsum(q_lens)
+    c["qs"] = qs
+    c["Q"] = random_storage(rng, (int(qs[-1]), c["Hq"], c["d"]), c["dtype"])
+    return c
+
+
+def _prefill(oracle, c, **over):
+    args = dict(dtype=c["dtype"], num_kv_heads=c["Hkv"], block_size=c["B"], head_dim=c["d"])
+    args.update(over)
+    return oracle.paged_prefill_ref(c["Q"], c["k_pool"], c["v_pool"], c["tables"], c["qs"],
+                                    c["ctx"], c["scale"], **args)
+
+
+def pin_prefill_sdpa(oracle):
+    """Against torch's scaled_dot_product_attention in float64 with an explicit causal mask
+    (query j of a chunk of q_len at the end of ctx tokens sees tokens 0 .. ctx - q_len + j)."""
+    rng = np.random.default_rng(71)
+    cases = [
+        dict(dtype="f32", S=2, Hq=4, Hkv=4, d=64, ctx=(40, 17), q_lens=(40, 17)),
+        dict(dtype="bf16", S=3, Hq=8, Hkv=2, d=128, ctx=(33, 70, 16), q_lens=(33, 9, 1)),
+        dict(dtype="f16", S=2, Hq=6, Hkv=3, d=64, B=8, ctx=(50, 23), q_lens=(20, 23)),
+        dict(dtype="bf16", S=1, Hq=4, Hkv=1, d=128, B=32, ctx=(100,), q_lens=(64,)),
+    ]
+    for kw in cases:
+        c = _prefill_case(rng, **kw)
+        mine = _prefill(oracle, c)
+        scale = float(c["scale"])
+        for s in range(c["S"]):
+            n = int(c["ctx"][s])
+            ql = int(c["qs"][s + 1] - c["qs"][s])
+            q = _widen_torch(c["Q"][c["qs"][s]:c["qs"][s + 1]], c["dtype"]).permute(1, 0, 2)[None]
+            K = _widen_torch(c["K"][s], c["dtype"]).permute(1, 0, 2)[None].contiguous()
+            V = _widen_torch(c["V"][s], c["dtype"]).permute(1, 0, 2)[None].contiguous()
+            mask = (torch.arange(n)[None, :] <= (n - ql + torch.arange(ql))[:, None])
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q, K, V, attn_mask=mask, scale=scale, enable_gqa=c["Hq"] != c["Hkv"])[0]
+            for j in range(ql):
+                assert np.abs(mine[(s, j)] - o[:, j, :].numpy()).max() <= 1e-12, (kw, s, j)
+
+
+def pin_prefill_decode_and_chunks(oracle):
+    """One query per sequence is a decode step; a prompt taken in two chunks (the second chunk's
+    queries over the whole context) gives the whole prompt's rows exactly."""
+    rng = np.random.default_rng(73)
+    c = _prefill_case(rng, dtype="bf16", S=3, Hq=4, Hkv=2, d=64, ctx=(30, 1, 65),
+                      q_lens=(1, 1, 1))
+    c["q"] = c["Q"]  # one query row per sequence
+    dec = decode(oracle, c)
+    pre = _prefill(oracle, c)
+    for s in range(3):
+        assert np.array_equal(pre[(s, 0)], dec[s])
+    n, n1 = 45, 19
+    whole = _prefill_case(np.random.default_rng(75), dtype="f16", S=1, Hq=4, Hkv=2, d=64,
+                          ctx=(n,), q_lens=(n,))
+    full = _prefill(oracle, whole)
+    tail = dict(whole)
+    tail["Q"] = whole["Q"][n1:]
+    tail["qs"] = np.array([0, n - n1], np.int32)
+    part = _prefill(oracle, tail)
+    for j in range(n - n1):
+        assert np.array_equal(part[(0, j)], full[(0, n1 + j)])
+    # the first query of a whole prompt sees only itself: its output is its own value row
+    v0 = oracle.to_f64(whole["V"][0][0], "f16")
+    for h in range(4):
+        assert np.array_equal(full[(0, 0)][h], v0[h // 2])
+
+
+def pin_swap_blocks(oracle):
+    """Swapping blocks into another pool changes exactly the destination blocks, each becoming
+    a bit copy of its source block in both pools; swapping out and back in restores the blocks;
+    within one pool it is the copy-on-write copy."""
+    rng = np.random.default_rng(77)
+    kw = dict(dtype="bf16", num_kv_heads=2, block_size=16, head_dim=64)
+    shape = (2, 16 * 64)
+    gk, gv = (random_storage(rng, (12,) + shape, "bf16") for _ in range(2))
+    hk, hv = (random_storage(rng, (7,) + shape, "bf16") for _ in range(2))
+    pairs = np.array([[3, 6], [11, 0], [4, 2]], np.int32)
+    ok, ov = oracle.swap_blocks_ref(hk, hv, gk, gv, pairs, **kw)
+    changed = sorted(set(range(7)) - {b for b in range(7) if np.array_equal(ok[b], hk[b])
+                                        and np.array_equal(ov[b], hv[b])})
+    assert changed == [0, 2, 6]
+    for src, dst in pairs:
+        assert np.array_equal(ok[dst], gk[src]) and np.array_equal(ov[dst], gv[src])
+    back_k, back_v = oracle.swap_blocks_ref(np.zeros_like(gk), np.zeros_like(gv), ok, ov,
+                                            pairs[:, ::-1], **kw)
+    for src, _ in pairs:
+        assert np.array_equal(back_k[src], gk[src]) and np.array_equal(back_v[src], gv[src])
+    within = oracle.swap_blocks_ref(gk, gv, gk, gv, np.array([[1, 5]], np.int32), **kw)
+    cow = oracle.copy_blocks_ref(gk, gv, np.array([[1, 5]], np.int32), **kw)
+    assert all(np.array_equal(a, b) for a, b in zip(within, cow))
+
+
 ALL_PINS = [pin_widening, pin_layout, pin_slot_enumeration, pin_cache_round_trip,
             pin_cache_write_footprint, pin_copy_blocks, pin_sdpa, pin_closed_forms,
             pin_paging_invariance, pin_block_size_invariance, pin_sharing_invariance,
-            pin_poison_ignored, pin_blockwise_online, pin_split_merge]
+            pin_poison_ignored, pin_blockwise_online, pin_split_merge, pin_prefill_sdpa,
+            pin_prefill_decode_and_chunks, pin_swap_blocks]

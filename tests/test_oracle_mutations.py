@@ -174,10 +174,50 @@ def m_bf16_shift(mp):
     _patch(mp, "to_f64", f)
 
 
+def _prefill_with(mp, limit):
+    """paged_prefill_ref with the last visible token of query j (chunk of q_len at the end of
+    ctx tokens) given by limit(ctx, q_len, j) instead of ctx - q_len + j."""
+    def f(query, k_pool, v_pool, block_tables, query_start, context_lens, scale, *, dtype,
+          num_kv_heads, block_size, head_dim, seqs=None, rows=None):
+        q64 = pa_mod.to_f64(query, dtype)
+        T, Hq, d = q64.shape
+        G = Hq // num_kv_heads
+        scale64 = float(np.float32(scale))
+        out = {}
+        for s in (range(len(context_lens)) if seqs is None else seqs):
+            ctx = int(context_lens[s])
+            q0, q1 = int(query_start[s]), int(query_start[s + 1])
+            K, V = pa_mod.gather_sequence_kv(k_pool, v_pool, block_tables[s], ctx, dtype=dtype,
+                                             num_kv_heads=num_kv_heads, block_size=block_size,
+                                             head_dim=head_dim)
+            for j in range(q1 - q0):
+                p = limit(ctx, q1 - q0, j)
+                out[(s, j)] = np.stack([pa_mod.attention_one_query(
+                    q64[q0 + j, h], K[:p + 1, h // G], V[:p + 1, h // G], scale64)
+                    for h in range(Hq)])
+        return out
+    _patch(mp, "paged_prefill_ref", f)
+
+
+def m_prefill_sees_next_token(mp):
+    _prefill_with(mp, lambda ctx, ql, j: min(ctx - ql + j + 1, ctx - 1))
+
+
+def m_prefill_ignores_chunk_offset(mp):
+    _prefill_with(mp, lambda ctx, ql, j: j)
+
+
+def m_swap_reads_destination_pool(mp):
+    def f(dst_k, dst_v, src_k, src_v, pairs, **kw):
+        return _orig["swap_blocks_ref"](dst_k, dst_v, dst_k, dst_v, pairs, **kw)
+    _patch(mp, "swap_blocks_ref", f)
+
+
 MUTATIONS = [m_exp_sign, m_denominator, m_keys_as_values, m_no_scale, m_scale_twice,
              m_head_modulo, m_gather_block_index, m_gather_slot_index, m_gather_one_past,
              m_k_offset_swapped, m_v_offset_transposed, m_slot_swapped, m_copy_only_keys,
-             m_merge_no_rescale_l, m_online_no_rescale, m_bf16_shift]
+             m_merge_no_rescale_l, m_online_no_rescale, m_bf16_shift, m_prefill_sees_next_token,
+             m_prefill_ignores_chunk_offset, m_swap_reads_destination_pool]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__ for m in MUTATIONS])
