@@ -196,6 +196,69 @@ def swap_rate(cfg, batch, v, stream, reps=5):
     return res
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense 16-bit matrix-core peak
+
+
+def prefill_rate(name, steps, warmup, stream):
+    """pa_prefill on a prefill workload: the new tokens' cache write, then the causal attention
+    of every new token, K calls each with HIP events on the launch stream. The attention is two
+    dense products per key/value tile on the matrix cores, so its roofline is the 16-bit MFMA
+    peak, with the flops counted from the causal definition (no masked or padded work)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_384_amd as pa
+    from paged_kv_cache_384_amd import workloads as wl
+    cfg = wl.PREFILL_CONFIGS[name]
+    batch = wl.build_batch(cfg)
+    dev = torch.device("cuda:0")
+    v = wl.make_values(batch, device=dev, seed=0, poison_nan=False)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    ctx = torch.from_numpy(batch.context_lens).to(dev)
+    qs = torch.from_numpy(batch.query_start).to(dev)
+    tseq = torch.from_numpy(batch.token_seq).to(dev)
+    tpos = torch.from_numpy(batch.token_pos).to(dev)
+    out = torch.empty_like(v["query"])
+
+    def write():
+        pa.pa_reshape_and_cache(v["k_pool"], v["v_pool"], v["key"], v["value"], bt, tseq, tpos)
+
+    def attend():
+        pa.pa_prefill(out, v["query"], v["k_pool"], v["v_pool"], bt, qs, ctx, cfg.scale,
+                      batch.max_query_len, batch.max_context_len)
+
+    for _ in range(max(1, warmup)):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        write()
+        e[1].record(stream)
+        attend()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    w_us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+    a_list = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    a_us = float(np.mean(a_list))
+    flops = batch.attention_flops()
+    tf = flops / (a_us * 1e-6) / 1e12
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    new_tokens = int(batch.query_lens.sum())
+    print(f"[bench] prefill {name}: attention {a_us:.1f} us (p10 {np.percentile(a_list, 10):.1f}, "
+          f"p90 {np.percentile(a_list, 90):.1f}) = {tf:.1f} TFLOP/s ({tf / peak:.3f} of peak), "
+          f"cache write {w_us:.1f} us", file=sys.stderr, flush=True)
+    return {"workload": name, "description": cfg.description, "dtype": cfg.dtype,
+            "new_tokens": new_tokens, "context_tokens": int(batch.context_lens.sum()),
+            "attention_us": round(a_us, 2), "cache_write_us": round(w_us, 2),
+            "tokens_per_s": round(new_tokens / ((a_us + w_us) * 1e-6), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                         "kernel": "prefill_kernel", "avg_us": round(a_us, 2),
+                         "flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +281,11 @@ def main():
     ap.add_argument("--swap", action="store_true",
                     help="also time swapping every block of half the sequences out to pinned "
                          "host memory and back (pa_swap_blocks)")
+    ap.add_argument("--prefill", default="",
+                    help="comma-separated prefill workloads to time as well (pa_prefill), e.g. "
+                         "prefill_bf16,chunked_fp16")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the --prefill workloads and print their JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -236,6 +304,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    prefill_names = [n for n in args.prefill.split(",") if n]
+    if args.prefill_only:
+        stream = torch.cuda.current_stream(dev)
+        res = [prefill_rate(n, args.steps, args.warmup, stream) for n in prefill_names]
+        print(json.dumps({"prefill": res}), flush=True)
+        return
     cfg = wl.CONFIGS[args.config]
     if args.block_size and args.block_size != cfg.block_size:
         cfg = wl.config(args.config, block_size=args.block_size, num_blocks=0)
@@ -358,6 +432,8 @@ def main():
     if args.paging_overhead:
         paging = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream)
 
+    prefill = [prefill_rate(n, args.steps, args.warmup, stream) for n in prefill_names]
+
     cpu = None
     if not args.no_cpu_baseline:
         host = {name: host_storage(sets[0][name]) for name in ("query", "k_pool", "v_pool")}
@@ -398,6 +474,8 @@ def main():
         line["paging_overhead"] = paging
     if swap is not None:
         line["swap"] = swap
+    if prefill:
+        line["prefill"] = prefill
     print(json.dumps(line), flush=True)
 
 

@@ -1,5 +1,5 @@
 /*
- * pa.h — paged KV-cache decode attention for AMD Instinct MI355X (gfx950, CDNA4).
+ * pa.h — paged KV-cache attention (decode and prefill) for AMD Instinct MI355X (gfx950, CDNA4).
  *
  * Plain C ABI: raw pointers and sizes, no HIP or PyTorch types. Streams are hipStream_t
  * handles passed as void* (NULL = the default stream). All device buffers are owned by the
@@ -62,7 +62,7 @@ extern "C" {
 #define PA_API
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -209,6 +209,50 @@ PA_API pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_ca
                                int32_t num_seqs, int32_t num_q_heads, float scale,
                                int32_t max_context_len, int32_t partition_size, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill — causal attention of many new query tokens per sequence over its paged KV cache
+ * (a prompt, or a chunk of one, whose keys and values pa_reshape_and_cache has already written).
+ * ([wiki] the dense causal form for a general query token i and its blocked form over the first
+ *  ceil(i/B) blocks; pa_decode is the case of one query per sequence.)
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1: its newest
+ * q_len = query_start[s+1] - query_start[s] tokens, so with n = context_lens[s] cached tokens
+ * (those q_len included) its query j sits at position p = n - q_len + j. For query head h (KV
+ * head g = h / G):
+ *     z_t = scale * dot(query[row][h], K_t) for t in [0, p],   out[row][h] = sum_t softmax(z)_t V_t
+ * with token t at physical block block_tables[s][t / B], slot t % B. Nothing past position p is
+ * read into the result; slots past n and table entries past ceil(n / B) are never read. Products
+ * are formed on the matrix cores from the 16-bit inputs and summed in fp32; the softmax weights
+ * are rounded to c->dtype before they multiply the values (as in the usual flash-attention
+ * form); out is rounded to c->dtype (nearest even).
+ *
+ *   key_cache, value_cache  device pools (layout above), read only
+ *   out, query              device [T][num_q_heads][d], c->dtype, T = query_start[num_seqs]
+ *   block_tables            device int32 [num_seqs][max_blocks_per_seq]
+ *   query_start             device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
+ *   context_lens            device int32 [num_seqs]
+ *   scale                   softmax scale (1/sqrt(d) in the usual case)
+ *   max_query_len           host-side upper bound of every q_len (sizes the grid: one workgroup
+ *                           per 128 queries of each (sequence, query head)); queries past it
+ *                           are not computed and their rows of out are left as they were
+ *   max_context_len         host-side upper bound of context_lens, <= max_blocks_per_seq * B;
+ *                           a context above it is truncated to it
+ * Supported: PA_F16 and PA_BF16 (PA_F32 gives PA_ERR_UNSUPPORTED), head_dim 64 or 128, block
+ * sizes 8, 16, 32; PA_CACHE_SHARED_BLOCKS is accepted and changes nothing (tiles are always read
+ * through the caches: every query tile of a sequence reads its blocks).
+ * Errors: checked on the host before the launch (PA_ERR_NULL / SHAPE / UNSUPPORTED / ALIGN); a
+ * failed launch gives PA_ERR_LAUNCH. num_seqs = 0 or max_query_len = 0 returns PA_OK.
+ * Caller contract (not checked on the device beyond clamping): q_len <= n; a query whose
+ * position would be negative (q_len > n) gets a zero row. A block id outside [0, NB) is clamped
+ * into range (no fault, but the result is then meaningless).
+ */
+PA_API pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
+                            void* out, const void* query, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* query_start,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            float scale, int32_t max_query_len, int32_t max_context_len,
+                            void* stream);
 
 /*
  * pa_copy_blocks — duplicate whole physical blocks (copy-on-write).

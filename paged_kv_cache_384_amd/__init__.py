@@ -1,4 +1,4 @@
-"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+"""Paged KV-cache attention (decode and prefill) for AMD Instinct MI355X (gfx950).
 
 A thin ctypes binding over the C ABI of ``libpa.so`` (declared in ``include/pa.h``). The
 functions keep the C names and only marshal arguments: torch tensors become device pointers,
@@ -8,6 +8,8 @@ kernels; there is no fallback. If the library is not built, the first call raise
     pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token_seq, token_pos)
     pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
               max_context_len, partition_size=0, workspace=None)
+    pa_prefill(out, query, key_cache, value_cache, block_tables, query_start, context_lens,
+               scale, max_query_len, max_context_len)
     pa_copy_blocks(key_cache, value_cache, src_dst)
 
 Pools are tensors of shape [num_blocks, num_kv_heads, block_size * head_dim] in the element
@@ -21,11 +23,11 @@ import os
 
 __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
-    "pa_decode_reduce", "pa_decode_contiguous", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
+    "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +35,8 @@ library_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
-                    "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_abi_version"]
+                    "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string",
+                    "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -76,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_contiguous.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                            ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t, _vp]
         L.pa_decode_contiguous.restype = ctypes.c_int
+        L.pa_prefill.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                 ctypes.c_float, _i32, _i32, _vp]
+        L.pa_prefill.restype = ctypes.c_int
         L.pa_swap_blocks.argtypes = [_desc_p, _vp, _vp, _desc_p, _vp, _vp, _vp, _i32, _vp]
         L.pa_swap_blocks.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_desc_p, _vp, _vp, _vp, _i32, _vp]
@@ -264,6 +270,33 @@ def pa_decode_contiguous(out, query, key_cache, value_cache, context_lens, scale
             int(max_context_len), int(partition_size), ws_ptr, ws_bytes, _stream(query, stream))
     _check(lib().pa_decode_contiguous(*args), "pa_decode_contiguous")
     return workspace
+
+
+def pa_prefill(out, query, key_cache, value_cache, block_tables, query_start, context_lens, scale,
+               max_query_len, max_context_len, *, block_size: int | None = None,
+               shared_blocks: bool = False, stream=None) -> None:
+    """Causal attention of every new query row over its sequence's paged cache.
+
+    query/out are [T, Hq, d]; sequence s owns rows query_start[s] .. query_start[s+1]-1, its
+    newest tokens, so its query j sits at position context_lens[s] - q_len + j.
+    """
+    import torch
+    T, Hq, head_dim = query.shape
+    d = _desc(key_cache, head_dim, block_size, shared_blocks)
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query in shape and dtype")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key and value pools differ in shape")
+    S = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]; query_start [num_seqs + 1]")
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache", query.dtype),
+            _dev(value_cache, "value_cache", query.dtype), _dev(out, "out"),
+            _dev(query, "query"), _dev(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev(query_start, "query_start", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32), S, Hq, float(scale),
+            int(max_query_len), int(max_context_len), _stream(query, stream))
+    _check(lib().pa_prefill(*args), "pa_prefill")
 
 
 def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size: int | None = None,

@@ -1,4 +1,4 @@
-// C ABI of the paged decode library: argument checks on the host, partition choice, dispatch.
+// C ABI of the paged attention library: argument checks on the host, partition choice, dispatch.
 // Every check runs before any launch; besides the launches and hipGetLastError the only HIP call
 // is pa_swap_blocks' pointer query (hipPointerGetAttributes). No device memory is allocated.
 #include <stdint.h>
@@ -260,6 +260,53 @@ pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_cache,
   return decode_impl(kStageAttention | kStageReduce, false, c, key_cache, value_cache, out, query,
                      nullptr, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
                      max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
+                     void* out, const void* query, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* query_start,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     float scale, int32_t max_query_len, int32_t max_context_len, void* stream) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (c->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+    return PA_ERR_SHAPE;
+  const int64_t tiles = (static_cast<int64_t>(max_query_len) + pa::kPrefillTileQueries - 1) /
+                        pa::kPrefillTileQueries;
+  const int64_t wgs = tiles * num_seqs * num_q_heads;
+  if (wgs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (wgs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !out || !query || !block_tables || !query_start ||
+      !context_lens)
+    return PA_ERR_NULL;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(out, 16) ||
+      !aligned(query, 16) || !aligned(block_tables, 4) || !aligned(query_start, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  pa::PrefillArgs a;
+  a.k_pool = static_cast<const uint8_t*>(key_cache);
+  a.v_pool = static_cast<const uint8_t*>(value_cache);
+  a.out = static_cast<uint8_t*>(out);
+  a.query = static_cast<const uint8_t*>(query);
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.max_ctx = max_context_len;
+  a.num_wgs = static_cast<int32_t>(wgs);
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  if (pa::launch_prefill(static_cast<DType>(c->dtype), c->head_dim, c->block_size, a,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
 }
 
 pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,

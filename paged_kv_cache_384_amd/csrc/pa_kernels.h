@@ -70,6 +70,30 @@ struct DecodeArgs {
                         // s * max_blocks + j (the contiguous twin)
 };
 
+constexpr int kPrefillThreads = 256;       // four wavefronts per prefill workgroup
+constexpr int kPrefillTileQueries = 128;  // queries one prefill workgroup owns
+constexpr int kPrefillTileTokens = 64;    // tokens per key/value tile of the prefill loop
+
+// One launch covers every (query tile of kPrefillTileQueries, sequence, query head).
+struct PrefillArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  uint8_t* out;
+  const uint8_t* query;  // [T][Hq][D], rows query_start[s] .. query_start[s+1]-1 of sequence s
+  const int32_t* block_tables;
+  const int32_t* query_start;  // [num_seqs + 1]
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_query_len;
+  int32_t max_ctx;
+  int32_t num_wgs;      // ceil(max_query_len / kPrefillTileQueries) * num_seqs * num_q_heads
+  float scale_log2;     // scale * log2(e)
+};
+
 // Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).
 hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
                                     const CacheWriteArgs& a, hipStream_t stream);
@@ -81,5 +105,7 @@ hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs&
 hipError_t launch_decode_attention_b32(DType dt, int head_dim, const DecodeArgs& a,
                                        hipStream_t stream);
 hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(DType dt, int head_dim, int block_size, const PrefillArgs& a,
+                          hipStream_t stream);
 
 }  // namespace pa

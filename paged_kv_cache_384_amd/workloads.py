@@ -1,5 +1,5 @@
-"""Seeded synthetic inputs for the paged decode path: configurations, a host block manager and
-value generators.
+"""Seeded synthetic inputs for the paged attention path (decode and prefill): configurations, a
+host block manager and value generators.
 
 This module is shared by the tests, the benchmark and the smoke check. It holds none of the
 path's arithmetic: no attention, no slot computation, no pool layout. It only
@@ -33,7 +33,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 __all__ = [
-    "DecodeConfig", "CONFIGS", "BlockManager", "PoolExhausted", "DecodeBatch", "build_batch",
+    "DecodeConfig", "CONFIGS", "PREFILL_CONFIGS", "BlockManager", "PoolExhausted", "DecodeBatch", "build_batch",
     "make_values", "config", "element_size", "kv_bytes_per_token",
 ]
 
@@ -66,6 +66,12 @@ class DecodeConfig:
     ``placement``: "shuffled" hands physical blocks out in a seeded random order; "contiguous"
     gives sequence s the span of physical blocks [s * W, s * W + ceil(ctx / B)) with W the
     table width (the layout of a cache that is not paged; the pool is S * W + 1 blocks).
+    ``new_tokens`` names how many of each context's tokens are new this step (written to the
+    cache and used as queries; they are always the newest):
+      ("one",)               one per sequence (a decode step)
+      ("all",)               the whole context (a prompt's prefill)
+      ("uniform", lo, hi)    integers in [lo, hi], capped at the context (a prefill chunk on
+                             top of tokens cached earlier)
     """
     name: str
     dtype: str
@@ -81,6 +87,7 @@ class DecodeConfig:
     partition_size: int = 0
     description: str = ""
     placement: str = "shuffled"
+    new_tokens: tuple = ("one",)
 
     @property
     def esz(self) -> int:
@@ -139,9 +146,26 @@ CONFIGS: dict[str, DecodeConfig] = {
 }
 
 
+# Prefill workloads (many new tokens per sequence): the attention becomes two dense products per
+# key/value tile, so these are measured in FLOP/s on the matrix cores rather than in HBM bytes.
+PREFILL_CONFIGS: dict[str, DecodeConfig] = {
+    "prefill_bf16": DecodeConfig(
+        "prefill_bf16", "bf16", num_seqs=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        ctx=("uniform", 512, 4096), new_tokens=("all",), seed=6,
+        description="GQA prompt prefill bf16: 16 prompts of U[512,4096] tokens, 32 q heads "
+                    "over 8 KV heads, d=128, B=16, every prompt token a query"),
+    "chunked_fp16": DecodeConfig(
+        "chunked_fp16", "f16", num_seqs=32, num_q_heads=40, num_kv_heads=40, head_dim=128,
+        ctx=("uniform", 512, 4096), new_tokens=("uniform", 128, 512), seed=7,
+        description="OPT-13B-shape chunked prefill fp16: 32 seqs with contexts U[512,4096], "
+                    "of which the newest U[128,512] tokens are this step's queries, 40 heads, "
+                    "d=128, B=16"),
+}
+
+
 def config(name: str, **overrides) -> DecodeConfig:
     """A named configuration, optionally with fields replaced (for smaller parity cases)."""
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if name in CONFIGS else PREFILL_CONFIGS[name]
     return replace(cfg, **overrides) if overrides else cfg
 
 
@@ -283,11 +307,32 @@ class DecodeBatch:
     num_blocks: int
     poison_block: int               # physical block that no sequence owns
     copy_pairs: np.ndarray          # int32 [P, 2] (src, dst) copy-on-write pairs
-    token_seq: np.ndarray           # int32 [T] sequence of each new token
-    token_pos: np.ndarray           # int32 [T] position of each new token (ctx - 1)
+    token_seq: np.ndarray           # int32 [T] sequence of each new token (grouped by sequence)
+    token_pos: np.ndarray           # int32 [T] position of each new token (ctx - q_len .. ctx - 1)
     ref_counts: np.ndarray          # int64 [NB]
     wasted_slots: np.ndarray        # int64 [S]
+    query_lens: np.ndarray          # int32 [S] new tokens (queries) per sequence
     extra: dict = field(default_factory=dict)
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """int32 [S + 1]: sequence s's new tokens are rows query_start[s] .. query_start[s+1]-1."""
+        return np.concatenate([[0], np.cumsum(self.query_lens, dtype=np.int64)]).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.query_lens.size else 0
+
+    def attention_flops(self) -> int:
+        """Multiply-adds x 2 of the two products of causal attention over every new token:
+        query j of a sequence with n cached tokens and q new ones sees n - q + j + 1 tokens, and
+        each seen token costs d multiply-adds for its score and d for its share of the output,
+        per query head."""
+        c = self.cfg
+        n = self.context_lens.astype(np.int64)
+        q = self.query_lens.astype(np.int64)
+        seen = q * (n - q) + q * (q + 1) // 2  # sum over j of (n - q + j + 1)
+        return int(seen.sum()) * 4 * c.head_dim * c.num_q_heads
 
     @property
     def max_context_len(self) -> int:
@@ -392,11 +437,32 @@ def build_batch(cfg: DecodeConfig) -> DecodeBatch:
     ref[poison] = 0
     pairs = np.array(bm.copies, dtype=np.int32).reshape(-1, 2)
     waste = np.array([bm.wasted_slots(s) for s in seqs], dtype=np.int64)
+    qlens = _draw_query_lens(cfg, lens)
+    token_seq = np.repeat(np.arange(S, dtype=np.int32), qlens)
+    token_pos = np.concatenate([np.arange(int(n) - int(q), int(n), dtype=np.int32)
+                                for n, q in zip(lens, qlens)] or [np.zeros(0, np.int32)])
     return DecodeBatch(
         cfg=cfg, context_lens=lens, block_tables=tables, num_blocks=nb_pool,
-        poison_block=int(poison), copy_pairs=pairs,
-        token_seq=np.arange(S, dtype=np.int32), token_pos=(lens - 1).astype(np.int32),
-        ref_counts=ref, wasted_slots=waste)
+        poison_block=int(poison), copy_pairs=pairs, token_seq=token_seq,
+        token_pos=token_pos.astype(np.int32), ref_counts=ref, wasted_slots=waste,
+        query_lens=qlens)
+
+
+def _draw_query_lens(cfg: DecodeConfig, lens: np.ndarray) -> np.ndarray:
+    """New tokens per sequence (from a generator of its own, so the rest of the batch does not
+    depend on the choice)."""
+    kind = cfg.new_tokens[0]
+    if kind == "one":
+        # one per sequence even at ctx = 0 (its cache write has position -1 and is skipped)
+        return np.ones(len(lens), dtype=np.int32)
+    if kind == "all":
+        return lens.astype(np.int32)
+    if kind == "uniform":
+        lo, hi = cfg.new_tokens[1:]
+        rng = np.random.default_rng([cfg.seed, 101])
+        q = rng.integers(lo, hi + 1, size=len(lens))
+        return np.minimum(q, lens).astype(np.int32)
+    raise ValueError(kind)
 
 
 def _torch_dtype(dtype: str):
@@ -408,7 +474,8 @@ def make_values(batch: DecodeBatch, device="cpu", seed: int | None = None, poiso
     """N(0,1) query, new-token key/value and pool contents, rounded (nearest-even) to the dtype.
 
     Returns a dict of torch tensors on ``device``:
-      query [S, Hq, d], key/value [T, Hkv, d], k_pool/v_pool [NB, Hkv, B*d].
+      query [T, Hq, d], key/value [T, Hkv, d], k_pool/v_pool [NB, Hkv, B*d], with T the number
+      of new tokens (one per sequence in a decode step, so query is then [S, Hq, d]).
     With ``poison_nan`` the poison block (where every unused table entry points) is NaN, so a
     read past a sequence's last block shows up in the result.
     """
@@ -425,7 +492,7 @@ def make_values(batch: DecodeBatch, device="cpu", seed: int | None = None, poiso
         return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(tdt)
 
     out = {
-        "query": draw(S, Hq, d),
+        "query": draw(T, Hq, d),
         "key": draw(T, Hkv, d),
         "value": draw(T, Hkv, d),
     }

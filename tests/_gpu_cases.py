@@ -1,9 +1,10 @@
-"""One decode step through the HIP library (C ABI via the ctypes binding) and through the CPU
-oracle on the same seeded inputs, with the comparisons the parity tests make.
+"""One decode or prefill step through the HIP library (C ABI via the ctypes binding) and
+through the CPU oracle on the same seeded inputs, with the comparisons the parity tests make.
 
-A step is: copy_blocks for the copy-on-write pairs, reshape_and_cache of one new token per
-sequence at position ctx - 1, then decode over ctx tokens. Cache writes and copies are compared
-bit for bit over the whole pools; attention within the stated tolerance.
+A step is: copy_blocks for the copy-on-write pairs, reshape_and_cache of the new tokens (one per
+sequence at position ctx - 1 for decode, the newest q_len for prefill), then the attention over
+ctx tokens. Cache writes and copies are compared bit for bit over the whole pools; attention
+within the stated tolerance.
 """
 from __future__ import annotations
 
@@ -58,6 +59,62 @@ def same_bits(a: np.ndarray, b: np.ndarray, dtype: str) -> bool:
     return np.array_equal(a.view(U[dtype]), b.view(U[dtype]))
 
 
+class Prepared:
+    """A batch, its seeded values as host storage arrays (pools with poisoned tails) and the
+    same on the GPU."""
+
+    def __init__(self, cfg, *, device_values=False, poison=True, value_seed=0):
+        dev = torch.device("cuda:0")
+        self.cfg = cfg
+        self.batch = batch = wl.build_batch(cfg)
+        vals = wl.make_values(batch, device=dev if device_values else "cpu", seed=value_seed)
+        kp = to_storage(vals["k_pool"])
+        vp = to_storage(vals["v_pool"])
+        if poison:
+            kp, vp = poison_tails(batch, kp, vp)
+        self.kp, self.vp = kp, vp
+        self.q = to_storage(vals["query"])
+        self.key = to_storage(vals["key"])
+        self.val = to_storage(vals["value"])
+        self.dt = cfg.dtype
+        tdt = vals["query"].dtype
+
+        def up(a):
+            return (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt)
+                    if self.dt == "bf16" else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+
+        self.kp_d, self.vp_d = up(kp), up(vp)
+        self.q_d, self.key_d, self.val_d = up(self.q), up(self.key), up(self.val)
+        self.bt_d = torch.from_numpy(batch.block_tables).to(dev)
+        self.ctx_d = torch.from_numpy(batch.context_lens).to(dev)
+        self.seq_d = torch.from_numpy(batch.token_seq).to(dev)
+        self.pos_d = torch.from_numpy(batch.token_pos).to(dev)
+        self.qs_d = torch.from_numpy(batch.query_start).to(dev)
+        self.pairs_d = torch.from_numpy(batch.copy_pairs.reshape(-1)).to(dev)
+        self.kw = dict(dtype=self.dt, num_kv_heads=cfg.num_kv_heads, block_size=cfg.block_size,
+                       head_dim=cfg.head_dim)
+
+    def write_cache(self, check_pools=True):
+        """Copy-on-write copies, then the new tokens into their slots, on both sides."""
+        batch, dt, kw = self.batch, self.dt, self.kw
+        if batch.copy_pairs.shape[0]:
+            pa.pa_copy_blocks(self.kp_d, self.vp_d, self.pairs_d, head_dim=self.cfg.head_dim)
+            torch.cuda.synchronize()
+            self.kp, self.vp = oracle.copy_blocks_ref(self.kp, self.vp, batch.copy_pairs, **kw)
+            if check_pools:
+                assert same_bits(to_storage(self.kp_d), self.kp, dt), "copy_blocks: key pool differs"
+                assert same_bits(to_storage(self.vp_d), self.vp, dt), "copy_blocks: value pool differs"
+        pa.pa_reshape_and_cache(self.kp_d, self.vp_d, self.key_d, self.val_d, self.bt_d,
+                                self.seq_d, self.pos_d)
+        torch.cuda.synchronize()
+        self.kp, self.vp = oracle.reshape_and_cache_ref(
+            self.kp, self.vp, self.key, self.val, batch.block_tables, batch.token_seq,
+            batch.token_pos, **kw)
+        if check_pools:
+            assert same_bits(to_storage(self.kp_d), self.kp, dt), "reshape_and_cache: key pool differs"
+            assert same_bits(to_storage(self.vp_d), self.vp, dt), "reshape_and_cache: value pool differs"
+
+
 def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=True,
              check_pools=True, value_seed=0, shared_blocks=None, twin=False):
     """Run one step on the GPU and check it against the oracle.
@@ -70,74 +127,82 @@ def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=
     require it to give pa_decode's output bit for bit.
     Returns a dict of measured errors.
     """
-    dev = torch.device("cuda:0")
     t0 = time.time()
-    batch = wl.build_batch(cfg)
-    vals = wl.make_values(batch, device=dev if device_values else "cpu", seed=value_seed)
-    kp = to_storage(vals["k_pool"])
-    vp = to_storage(vals["v_pool"])
-    if poison:
-        kp, vp = poison_tails(batch, kp, vp)
-    q = to_storage(vals["query"])
-    key = to_storage(vals["key"])
-    val = to_storage(vals["value"])
-    dt = cfg.dtype
-    tdt = vals["query"].dtype
-
-    def up(a):
-        return (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt)
-                if dt == "bf16" else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
-
-    kp_d, vp_d = up(kp), up(vp)
-    q_d, key_d, val_d = up(q), up(key), up(val)
-    bt_d = torch.from_numpy(batch.block_tables).to(dev)
-    ctx_d = torch.from_numpy(batch.context_lens).to(dev)
-    seq_d = torch.from_numpy(batch.token_seq).to(dev)
-    pos_d = torch.from_numpy(batch.token_pos).to(dev)
-    pairs_d = torch.from_numpy(batch.copy_pairs.reshape(-1)).to(dev)
-    kw = dict(dtype=dt, num_kv_heads=cfg.num_kv_heads, block_size=cfg.block_size,
-              head_dim=cfg.head_dim)
+    P = Prepared(cfg, device_values=device_values, poison=poison, value_seed=value_seed)
+    batch, dt = P.batch, P.dt
     res = {"prep_s": time.time() - t0}
-
-    # 1. copy-on-write copies
-    if batch.copy_pairs.shape[0]:
-        pa.pa_copy_blocks(kp_d, vp_d, pairs_d, head_dim=cfg.head_dim)
-        torch.cuda.synchronize()
-        kp, vp = oracle.copy_blocks_ref(kp, vp, batch.copy_pairs, **kw)
-        if check_pools:
-            assert same_bits(to_storage(kp_d), kp, dt), "copy_blocks: key pool differs"
-            assert same_bits(to_storage(vp_d), vp, dt), "copy_blocks: value pool differs"
-    # 2. new tokens into their slots
-    pa.pa_reshape_and_cache(kp_d, vp_d, key_d, val_d, bt_d, seq_d, pos_d)
-    torch.cuda.synchronize()
-    kp, vp = oracle.reshape_and_cache_ref(kp, vp, key, val, batch.block_tables, batch.token_seq,
-                                          batch.token_pos, **kw)
-    if check_pools:
-        assert same_bits(to_storage(kp_d), kp, dt), "reshape_and_cache: key pool differs"
-        assert same_bits(to_storage(vp_d), vp, dt), "reshape_and_cache: value pool differs"
+    # 1. copy-on-write copies, 2. new tokens into their slots
+    P.write_cache(check_pools)
     # 3. attention
-    out_d = torch.full_like(q_d, float("nan"))
+    out_d = torch.full_like(P.q_d, float("nan"))
     if shared_blocks is None:
         shared_blocks = batch.shares_blocks
-    pa.pa_decode(out_d, q_d, kp_d, vp_d, bt_d, ctx_d, cfg.scale, batch.max_context_len,
+    pa.pa_decode(out_d, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.ctx_d, cfg.scale, batch.max_context_len,
                  partition_size, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     if twin:
-        out2_d = torch.full_like(q_d, float("nan"))
-        pa.pa_decode_contiguous(out2_d, q_d, kp_d, vp_d, ctx_d, cfg.scale, batch.max_context_len,
-                                batch.max_blocks_per_seq, partition_size)
+        out2_d = torch.full_like(P.q_d, float("nan"))
+        pa.pa_decode_contiguous(out2_d, P.q_d, P.kp_d, P.vp_d, P.ctx_d, cfg.scale,
+                                batch.max_context_len, batch.max_blocks_per_seq, partition_size)
         torch.cuda.synchronize()
         assert same_bits(to_storage(out2_d), to_storage(out_d), dt), "contiguous twin differs"
     out = to_storage(out_d)
     seqs = list(range(cfg.num_seqs)) if sample is None else list(sample)
     t1 = time.time()
-    ref = oracle.paged_decode_ref(q, kp, vp, batch.block_tables, batch.context_lens, cfg.scale,
-                                  seqs=seqs, **kw)
+    ref = oracle.paged_decode_ref(P.q, P.kp, P.vp, batch.block_tables, batch.context_lens,
+                                  cfg.scale, seqs=seqs, **P.kw)
     res["oracle_s"] = time.time() - t1
     got = oracle.to_f64(out[seqs], dt)
     assert np.isfinite(got).all(), "non-finite output"
     err = float(np.abs(got - ref).max()) if ref.size else 0.0
     res["max_abs_err"] = err
     res["max_abs_out"] = float(np.abs(ref).max()) if ref.size else 0.0
+    assert err <= TOL[dt], f"{cfg.name}: max abs error {err} > {TOL[dt]}"
+    return res
+
+
+def run_prefill(cfg, *, rows=None, device_values=False, poison=True, check_pools=True,
+                value_seed=0, max_query_len=None, prepared=None):
+    """One prefill step on the GPU (cache writes of every new token, then pa_prefill) checked
+    against the oracle.
+
+    rows: None = every query row through the oracle; else a dict seq -> list of query indices j.
+    max_query_len: passed to pa_prefill (default: the batch's largest q_len); queries at or past
+    it must be left untouched (NaN in the output buffer).
+    Returns a dict of measured errors.
+    """
+    t0 = time.time()
+    P = prepared or Prepared(cfg, device_values=device_values, poison=poison,
+                             value_seed=value_seed)
+    batch, dt = P.batch, P.dt
+    res = {"prep_s": time.time() - t0}
+    P.write_cache(check_pools)
+    mql = batch.max_query_len if max_query_len is None else max_query_len
+    out_d = torch.full_like(P.q_d, float("nan"))
+    pa.pa_prefill(out_d, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d, P.ctx_d, cfg.scale, mql,
+                  batch.max_context_len)
+    torch.cuda.synchronize()
+    out = to_storage(out_d)
+    qs = batch.query_start
+    ql = batch.query_lens
+    if rows is None:
+        rows = {s: list(range(min(int(ql[s]), mql))) for s in range(cfg.num_seqs)}
+    rows = {s: [j for j in js if j < mql] for s, js in rows.items()}
+    t1 = time.time()
+    ref = oracle.paged_prefill_ref(P.q, P.kp, P.vp, batch.block_tables, qs, batch.context_lens,
+                                   cfg.scale, seqs=sorted(rows), rows=rows, **P.kw)
+    res["oracle_s"] = time.time() - t1
+    err, mx, n = 0.0, 0.0, 0
+    for (s, j), r in ref.items():
+        got = oracle.to_f64(out[int(qs[s]) + j], dt)
+        assert np.isfinite(got).all(), f"non-finite output at seq {s} query {j}"
+        err = max(err, float(np.abs(got - r).max()))
+        mx = max(mx, float(np.abs(r).max()))
+        n += 1
+    # rows past max_query_len are not computed
+    skipped = [int(qs[s]) + j for s in range(cfg.num_seqs) for j in range(mql, int(ql[s]))]
+    if skipped:
+        assert np.isnan(oracle.to_f64(out[skipped], dt)).all(), "rows past max_query_len written"
+    res.update(max_abs_err=err, max_abs_out=mx, rows=n)
     assert err <= TOL[dt], f"{cfg.name}: max abs error {err} > {TOL[dt]}"
     return res

@@ -222,3 +222,37 @@ def test_swap_validation(L):
     assert sw(desc(), desc(), GOOD, 2, dk=ODD) == ALIGN
     assert sw(desc(), desc(), P(0x10002), 2) == ALIGN
     assert sw(desc(), desc(), P(0), 0) == OK
+
+
+def test_prefill_validation(L):
+    """16-bit pools only; sizes, pointers and alignment checked before the launch."""
+    def pf(d=None, *, S=2, Hq=4, maxb=8, mql=100, max_ctx=100, ptrs=None):
+        d = desc() if d is None else d
+        p = ptrs or {}
+        return L.pa_prefill(ctypes.byref(d) if d is not False else None, p.get("k", GOOD),
+                            p.get("v", GOOD), p.get("out", GOOD), p.get("q", GOOD),
+                            p.get("bt", GOOD), maxb, p.get("qs", GOOD), p.get("ctx", GOOD), S, Hq,
+                            0.1, mql, max_ctx, P(0))
+    assert pf(False) == NULL
+    assert pf(desc(dtype=0)) == UNSUP                    # fp32 has no matrix-core prefill
+    assert pf(desc(d=96)) == UNSUP
+    assert pf(desc(b=64)) == UNSUP
+    assert pf(desc(flags=2)) == UNSUP
+    assert pf(Hq=6) == SHAPE                             # not a multiple of 4 KV heads
+    assert pf(Hq=0) == SHAPE
+    assert pf(S=-1) == SHAPE
+    assert pf(mql=-1) == SHAPE
+    assert pf(max_ctx=8 * 16 + 1) == SHAPE               # longer than the table
+    assert pf(maxb=0) == SHAPE
+    assert pf(S=1 << 20, Hq=1 << 10, mql=1 << 12) == SHAPE  # grid past 2^31 workgroups
+    for k in ("k", "v", "out", "q", "bt", "qs", "ctx"):
+        assert pf(ptrs={k: P(0)}) == NULL, k
+    for k in ("k", "v", "out", "q"):
+        assert pf(ptrs={k: P(0x10008)}) == ALIGN, k
+    for k in ("bt", "qs", "ctx"):
+        assert pf(ptrs={k: P(0x10002)}) == ALIGN, k
+    none = {k: P(0) for k in ("k", "v", "out", "q", "bt", "qs", "ctx")}
+    assert pf(S=0, ptrs=none) == OK
+    assert pf(mql=0, ptrs=none) == OK
+    assert pf(desc(dtype=2, d=64, b=8), S=0, max_ctx=64, ptrs=none) == OK
+    assert pf(desc(dtype=2, d=64, b=8), S=0, max_ctx=65, ptrs=none) == SHAPE

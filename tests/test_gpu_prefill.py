@@ -1,0 +1,91 @@
+"""Parity of pa_prefill (causal attention of many new query tokens per sequence over the paged
+cache) with the CPU oracle, through the C ABI.
+
+Each case runs a whole prefill step: the new tokens' keys and values are written with
+pa_reshape_and_cache (pools compared bit for bit), then pa_prefill is compared with
+oracle.paged_prefill_ref query by query within the 16-bit tolerance (1e-2 max abs). Slots past
+each context in its last block hold NaN, so a read past the end shows up. The small cases check
+every query; they span several 128-query tiles and 64-token key tiles with ragged tails, GQA and
+MHA, head_dim 64 and 128, block sizes 8/16/32, prompts (every token new) and chunks on top of an
+earlier context. The full-size workloads check a sample of queries, including the first and last
+of the longest sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_384_amd as pa
+from paged_kv_cache_384_amd import workloads as wl
+from _gpu_cases import Prepared, log, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, dtype, S, Hq, Hkv, d, B, ctx, new, seed):
+    return wl.DecodeConfig(name, dtype, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                           block_size=B, ctx=ctx, new_tokens=new, seed=seed)
+
+
+CASES = [
+    # prompts: q_len = ctx, lengths around the 64-token and 128-query tile edges
+    small("prompt_f16_d64", "f16", 4, 4, 2, 64, 16, ("fixed", (1, 64, 129, 333)), ("all",), 11),
+    small("prompt_bf16_d128", "bf16", 3, 8, 2, 128, 16, ("fixed", (127, 128, 300)), ("all",), 12),
+    # chunks on top of earlier context
+    small("chunk_bf16_b8", "bf16", 5, 8, 2, 128, 8, ("uniform", 100, 700), ("uniform", 1, 300), 13),
+    small("chunk_f16_b32", "f16", 5, 4, 4, 128, 32, ("uniform", 64, 600), ("uniform", 1, 260), 14),
+    small("chunk_bf16_d64_b32", "bf16", 4, 6, 3, 64, 32, ("uniform", 200, 500), ("uniform", 60, 200), 15),
+    # one query per sequence: the decode case
+    small("one_f16", "f16", 6, 8, 8, 128, 16, ("uniform", 1, 400), ("one",), 16),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_prefill_small(cfg):
+    log(f"[prefill] {cfg.name}: ctx={cfg.ctx} new={cfg.new_tokens}")
+    r = run_prefill(cfg)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} max|o|={r['max_abs_out']:.3g}")
+
+
+def test_prefill_max_query_len_truncates():
+    """Queries at or past max_query_len are left untouched; the others keep their positions
+    (they are still the newest q_len tokens of their sequence)."""
+    cfg = small("trunc_bf16", "bf16", 3, 4, 2, 128, 16, ("fixed", (200, 300, 90)),
+                ("uniform", 150, 250), 17)
+    log(f"[prefill] truncated max_query_len=130 {cfg.ctx}")
+    r = run_prefill(cfg, max_query_len=130)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g}")
+
+
+def test_prefill_empty_sequences_and_zero_len():
+    """Sequences without new tokens write nothing; max_query_len 0 launches nothing."""
+    cfg = small("empty_f16", "f16", 8, 4, 4, 64, 16, ("uniform", 1, 90), ("uniform", 0, 3), 18)
+    P = Prepared(cfg)
+    assert (P.batch.query_lens == 0).any() and (P.batch.query_lens > 0).any()
+    log(f"[prefill] q_lens {P.batch.query_lens.tolist()}")
+    r = run_prefill(cfg, prepared=P)
+    assert r["rows"] == int(P.batch.query_lens.sum())
+    out = torch.full_like(P.q_d, float("nan"))
+    pa.pa_prefill(out, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d, P.ctx_d, cfg.scale, 0,
+                  P.batch.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "chunked_fp16"])
+@pytest.mark.timeout(900)
+def test_prefill_full_size(name):
+    cfg = wl.PREFILL_CONFIGS[name]
+    P = Prepared(cfg, device_values=True)
+    b = P.batch
+    ql = b.query_lens
+    rng = np.random.default_rng(5)
+    longest = int(np.argmax(ql))
+    rows = {longest: sorted({0, 1, int(ql[longest]) - 1, int(ql[longest]) // 2} |
+                            set(rng.integers(0, ql[longest], 12).tolist()))}
+    for s in rng.choice(cfg.num_seqs, 4, replace=False).tolist():
+        rows.setdefault(s, [])
+        rows[s] = sorted(set(rows[s]) | set(rng.integers(0, ql[s], 8).tolist()) | {int(ql[s]) - 1})
+    log(f"[prefill full] {name}: {sum(len(v) for v in rows.values())} sampled rows")
+    r = run_prefill(cfg, rows=rows, prepared=P)
+    log(f"    max_abs_err={r['max_abs_err']:.3g} max|o|={r['max_abs_out']:.3g} "
+        f"oracle {r['oracle_s']:.1f}s")
