@@ -232,7 +232,7 @@ PA_API pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_ca
  *   block_tables            device int32 [num_seqs][max_blocks_per_seq]
  *   query_start             device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0
  *   context_lens            device int32 [num_seqs]
- *   scale                   softmax scale (1/sqrt(d) in the usual case)
+ *   scale                   softmax scale, finite and > 0 (1/sqrt(d) in the usual case)
  *   max_query_len           host-side upper bound of every q_len (sizes the grid: one workgroup
  *                           per 128 queries of each (sequence, query head)); queries past it
  *                           are not computed and their rows of out are left as they were

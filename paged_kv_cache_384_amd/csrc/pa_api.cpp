@@ -1,6 +1,7 @@
 // C ABI of the paged attention library: argument checks on the host, partition choice, dispatch.
 // Every check runs before any launch; besides the launches and hipGetLastError the only HIP call
 // is pa_swap_blocks' pointer query (hipPointerGetAttributes). No device memory is allocated.
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/pa.h"
@@ -271,6 +272,7 @@ pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* 
   if (st != PA_OK) return st;
   if (c->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!(scale > 0.0f) || scale == INFINITY) return PA_ERR_SHAPE;  // also rejects NaN
   if (max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
       static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
     return PA_ERR_SHAPE;

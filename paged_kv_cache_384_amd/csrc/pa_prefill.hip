@@ -24,13 +24,17 @@
 //   * online softmax per query (column), in the base-2 domain: causal mask on tiles that reach
 //     past a query's position, running maximum shared by the four lanes of a column, rescaling of
 //     the output only when the maximum grows by more than a slack of 2^8 (the final division by
-//     the running sum makes the result exact either way);
+//     the running sum makes the result exact either way). The running sum is one more matrix
+//     product (all-ones A times the packed weights), so it sums exactly the 16-bit weights that
+//     multiply the values;
 //   * O^T += V^T P^T: A = 16 dims x 32 tokens from the transposed value rows, B = the
 //     probabilities, packed to 16 bits straight from the S^T registers. Lane l's eight k values
 //     are tokens {4(l/16)+i, 16+4(l/16)+i} (i < 4) of a 32-token step; the value rows are stored
 //     in that order, so P never moves between lanes.
 // Tokens at or past the context length are zero in LDS (their table entries are never read), so
 // slots past the end of the last block do not matter, whatever they hold.
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -41,27 +45,25 @@ constexpr int kTileT = kPrefillTileTokens;   // tokens per key/value tile
 constexpr int kTileQ = kPrefillTileQueries;  // queries per workgroup
 constexpr int kWaveQ = 32;                   // queries per wavefront (two MFMA columns)
 constexpr float kRescaleSlackPf = 8.0f;      // log2 of the largest weight before a rescale
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 static_assert(kPrefillThreads / 64 * kWaveQ == kTileQ, "four wavefronts of 32 queries");
 static_assert(kTileT == 64, "the token permutation below covers two 32-token MFMA steps");
 
-// 16-bit packing of two probabilities (round to nearest even; both are finite and >= 0).
+// Two fp32 values rounded (nearest even) to the 16-bit type and packed, low half first: one
+// v_cvt_pk_{f16,bf16}_f32 on gfx950.
 template <DType dt> struct Pack2;
 template <> struct Pack2<DType::F16> {
   __device__ static __forceinline__ uint32_t run(float a, float b) {
-    f16x2 h;
-    h.x = static_cast<_Float16>(a);
-    h.y = static_cast<_Float16>(b);
-    return __builtin_bit_cast(uint32_t, h);
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
 };
 template <> struct Pack2<DType::BF16> {
-  __device__ static __forceinline__ uint32_t rne(float x) {
-    uint32_t u = f32_bits(x);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-  }
   __device__ static __forceinline__ uint32_t run(float a, float b) {
-    return rne(a) | (rne(b) << 16);
+    const float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
 };
 
@@ -142,11 +144,13 @@ void prefill_kernel(PrefillArgs a) {
   const int vtok = 2 * (tid & 31);
   const int vpc = tid >> 5;
   const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
-  // byte offset of (the block holding token t, this KV head); t is clamped to the context so
-  // table entries past it are never read
-  auto tile_of = [&](int t) -> int64_t {
+  // the table entry of token t (clamped to the context, so entries past it are never read), and
+  // the byte offset of (block b, this KV head) with b clamped into the pool
+  auto table_block = [&](int t) -> int {
     t = t < ctx ? t : ctx - 1;
-    int b = a.block_tables[table_row + t / B];
+    return a.block_tables[table_row + t / B];
+  };
+  auto tile_of = [&](int b) -> int64_t {
     b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
     return (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * G::kTileBytes;
   };
@@ -197,10 +201,20 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) o[qb][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.0f, 0.0f};
+  // Running sums of the weights, formed on the matrix cores from the same 16-bit weights that
+  // multiply the values (A = all ones), so numerator and denominator use identical weights; every
+  // element of lacc[qb] holds the sum for the lane's column.
+  f32x4 lacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+  const uint32_t one2 = Pack2<dt>::run(1.0f, 1.0f);
+  const u32x4 ones = {one2, one2, one2, one2};
   const float thresh = kRescaleSlackPf;
 
-  auto compute = [&](int buf, int T0, bool masked) {
+  // One key/value tile. Scores stay raw (unscaled) until the exponent, where one fma applies the
+  // scale and subtracts the running maximum; the maximum of scaled scores is the scale times the
+  // raw maximum because the scale is positive. kMasked: the tile reaches past some column's
+  // position, so tokens after it get -inf.
+  auto compute = [&](int buf, int T0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     // S^T blocks: st[qb][tb][i] = score of query 16qb+col, token T0 + 16tb + 4grp + i
     f32x4 st[2][4];
     const uint8_t* kb = k_s[buf] + col * kKRow + grp * 16;
@@ -218,20 +232,22 @@ void prefill_kernel(PrefillArgs a) {
     float mx[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int pq = base_p + wj0 + qb * 16 + col;  // this column's query position
-      float mq = -INFINITY;
+      if constexpr (kMasked) {
+        const int lim = base_p + wj0 + qb * 16 + col - T0 - grp * 4;  // last visible offset
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = st[qb][tb][i] * a.scale_log2;
-          if (masked) x = T0 + tb * 16 + grp * 4 + i <= pq ? x : -INFINITY;
-          st[qb][tb][i] = x;
-          mq = fmaxf(mq, x);
-        }
+          for (int i = 0; i < 4; ++i)
+            st[qb][tb][i] = tb * 16 + i <= lim ? st[qb][tb][i] : -INFINITY;
+      }
+      float mq = fmaxf(fmaxf(st[qb][0][0], st[qb][0][1]), fmaxf(st[qb][0][2], st[qb][0][3]));
+#pragma unroll
+      for (int tb = 1; tb < 4; ++tb)
+        mq = fmaxf(mq, fmaxf(fmaxf(st[qb][tb][0], st[qb][tb][1]),
+                             fmaxf(st[qb][tb][2], st[qb][tb][3])));
       mq = fmaxf(mq, __shfl_xor(mq, 16, 64));
       mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
-      mx[qb] = mq;
+      mx[qb] = mq * a.scale_log2;
     }
     if (__builtin_amdgcn_ballot_w64(mx[0] > m[0] + thresh || mx[1] > m[1] + thresh) != 0) {
 #pragma unroll
@@ -240,7 +256,7 @@ void prefill_kernel(PrefillArgs a) {
         // a column with nothing visible yet keeps m = -inf and a factor of 1
         const float corr = mn == -INFINITY ? 1.0f : exp2_fast(m[qb] - mn);
         m[qb] = mn;
-        lsum[qb] *= corr;
+        lacc[qb] *= corr;
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) o[qb][db] *= corr;
       }
@@ -249,15 +265,13 @@ void prefill_kernel(PrefillArgs a) {
     u32x4 pb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mref = m[qb] == -INFINITY ? 0.0f : m[qb];
+      const float neg_m = m[qb] == -INFINITY ? 0.0f : -m[qb];
       float pr[4][4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[tb][i] = exp2_fast(st[qb][tb][i] - mref);
-          lsum[qb] += pr[tb][i];
-        }
+        for (int i = 0; i < 4; ++i)
+          pr[tb][i] = exp2_fast(__builtin_fmaf(st[qb][tb][i], a.scale_log2, neg_m));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         pb[qb][ks].x = Pack2<dt>::run(pr[2 * ks][0], pr[2 * ks][1]);
@@ -267,6 +281,11 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     const uint8_t* vb = v_s[buf] + col * kVtRow + grp * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      lacc[0] = Mfma16x16x32<dt>::run(ones, pb[0][ks], lacc[0]);
+      lacc[1] = Mfma16x16x32<dt>::run(ones, pb[1][ks], lacc[1]);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -278,36 +297,43 @@ void prefill_kernel(PrefillArgs a) {
   };
 
   // ---- walk the tiles ----------------------------------------------------------------------
-  int64_t kt_next = 0, vt_next = 0;
+  // The block ids of tile i+2 are loaded while tile i is computed and turned into addresses only
+  // at step i+1, when the tile's own loads are issued, so no step waits on a table read.
   if (n_steps > 0) {
-    load_tile(tile_of(ktok), tile_of(vtok));
-    kt_next = tile_of(kTileT + ktok);
-    vt_next = tile_of(kTileT + vtok);
+    load_tile(tile_of(table_block(ktok)), tile_of(table_block(vtok)));
+    // Every load so far (the queries and tile 0) completes here. Without this explicit wait the
+    // compiler's wait-count analysis, which cannot see that the query registers are complete
+    // once the first tile is, waits for every in-flight tile load before each step's first
+    // matrix instruction.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     store_tile(0, 0);
-  }
-  __syncthreads();
-  const int wp_lo = base_p + wj0;  // every column of the wave sees tokens 0..wp_lo
-  const int wp_hi = base_p + wj1;  // no column sees a token past wp_hi
-  for (int step = 0; step < n_steps; ++step) {
-    const int T0 = step * kTileT;
-    const bool more = step + 1 < n_steps;
-    if (more) {
-      load_tile(kt_next, vt_next);
-      kt_next = tile_of(T0 + 2 * kTileT + ktok);
-      vt_next = tile_of(T0 + 2 * kTileT + vtok);
-    }
-    if (w_active && T0 <= wp_hi) compute(step & 1, T0, T0 + kTileT - 1 > wp_lo);
-    if (more) store_tile((step + 1) & 1, T0 + kTileT);
+    int kb_next = table_block(kTileT + ktok);
+    int vb_next = table_block(kTileT + vtok);
     __syncthreads();
+    const int wp_lo = base_p + wj0;  // every column of the wave sees tokens 0..wp_lo
+    const int wp_hi = base_p + wj1;  // no column sees a token past wp_hi
+    for (int step = 0; step < n_steps; ++step) {
+      const int T0 = step * kTileT;
+      const bool more = step + 1 < n_steps;
+      if (more) {
+        load_tile(tile_of(kb_next), tile_of(vb_next));
+        kb_next = table_block(T0 + 2 * kTileT + ktok);
+        vb_next = table_block(T0 + 2 * kTileT + vtok);
+      }
+      if (w_active && T0 <= wp_hi) {
+        if (T0 + kTileT - 1 > wp_lo) compute(step & 1, T0, std::true_type{});
+        else compute(step & 1, T0, std::false_type{});
+      }
+      if (more) store_tile((step + 1) & 1, T0 + kTileT);
+      __syncthreads();
+    }
   }
 
   // ---- normalise and store: lane holds dims 16db + 4grp .. +3 of query 16qb + col ---------
   if (!w_active) return;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = lsum[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lacc[qb][0];
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const int j = wj0 + qb * 16 + col;
     if (j >= q_len) continue;

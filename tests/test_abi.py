@@ -226,13 +226,13 @@ def test_swap_validation(L):
 
 def test_prefill_validation(L):
     """16-bit pools only; sizes, pointers and alignment checked before the launch."""
-    def pf(d=None, *, S=2, Hq=4, maxb=8, mql=100, max_ctx=100, ptrs=None):
+    def pf(d=None, *, S=2, Hq=4, maxb=8, mql=100, max_ctx=100, ptrs=None, scale=0.1):
         d = desc() if d is None else d
         p = ptrs or {}
         return L.pa_prefill(ctypes.byref(d) if d is not False else None, p.get("k", GOOD),
                             p.get("v", GOOD), p.get("out", GOOD), p.get("q", GOOD),
                             p.get("bt", GOOD), maxb, p.get("qs", GOOD), p.get("ctx", GOOD), S, Hq,
-                            0.1, mql, max_ctx, P(0))
+                            scale, mql, max_ctx, P(0))
     assert pf(False) == NULL
     assert pf(desc(dtype=0)) == UNSUP                    # fp32 has no matrix-core prefill
     assert pf(desc(d=96)) == UNSUP
@@ -244,6 +244,8 @@ def test_prefill_validation(L):
     assert pf(mql=-1) == SHAPE
     assert pf(max_ctx=8 * 16 + 1) == SHAPE               # longer than the table
     assert pf(maxb=0) == SHAPE
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        assert pf(scale=bad) == SHAPE, bad
     assert pf(S=1 << 20, Hq=1 << 10, mql=1 << 12) == SHAPE  # grid past 2^31 workgroups
     for k in ("k", "v", "out", "q", "bt", "qs", "ctx"):
         assert pf(ptrs={k: P(0)}) == NULL, k
