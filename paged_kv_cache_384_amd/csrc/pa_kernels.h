@@ -90,7 +90,10 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t max_query_len;
   int32_t max_ctx;
-  int32_t num_wgs;      // ceil(max_query_len / kPrefillTileQueries) * num_seqs * num_q_heads
+  int32_t group;        // query heads per KV head
+  int32_t q_tiles;      // ceil(max_query_len / kPrefillTileQueries)
+  int32_t num_units;    // q_tiles * num_seqs * num_kv_heads: (query tile, sequence, KV head)
+  int32_t num_wgs;      // num_units rounded up to a multiple of 8 (the XCDs), times group
   float scale_log2;     // scale * log2(e)
 };
 

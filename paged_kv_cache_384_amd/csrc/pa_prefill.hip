@@ -93,19 +93,27 @@ void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) uint8_t k_s[2][kTileT * kKRow];
   __shared__ __align__(16) uint8_t v_s[2][D * kVtRow];
 
-  // ---- which queries: heaviest tiles first, query heads of one KV head side by side -------
-  const int L = xcd_logical_index();
-  const int h = L % a.num_q_heads;
-  const int rest = L / a.num_q_heads;
-  const int s = rest % a.num_seqs;
-  const int rev = rest / a.num_seqs;
+  // ---- which queries ---------------------------------------------------------------------
+  // A unit is (query tile qt, sequence, KV head); its G query heads read the same key/value
+  // tiles. The hardware deals workgroups round-robin over the 8 XCDs (blockIdx % 8), each with
+  // its own L2: unit u goes to XCD u % 8, where its G heads run as consecutive workgroups and
+  // share that L2. Units are numbered from the highest query tile down, so the longest-running
+  // workgroups (the latest queries of a prompt see the most tokens) start first on every XCD.
+  const int group = a.group;
+  const int k8 = static_cast<int>(blockIdx.x >> 3);
+  const int u = (k8 / group) * 8 + static_cast<int>(blockIdx.x & 7);
+  if (u >= a.num_units) return;
+  const int h_in = k8 % group;
+  const int g_kv = u % a.num_kv_heads;
+  const int s = (u / a.num_kv_heads) % a.num_seqs;
+  const int qt = a.q_tiles - 1 - u / (a.num_kv_heads * a.num_seqs);
+  const int h = g_kv * group + h_in;
   const int q0 = a.query_start[s];
   int n_q = a.query_start[s + 1] - q0;
   n_q = n_q < 0 ? 0 : n_q;
   // queries past max_query_len are not computed; positions still count every query
   const int q_len = n_q > a.max_query_len ? a.max_query_len : n_q;
-  const int qt = (q_len + kTileQ - 1) / kTileQ - 1 - rev;
-  if (qt < 0) return;
+  if (qt * kTileQ >= q_len) return;
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int j0 = qt * kTileQ;
@@ -120,7 +128,7 @@ void prefill_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int col = lane & 15;  // MFMA column (query) / row (token, dim) within a 16-block
   const int grp = lane >> 4;  // MFMA lane group: k values 8*grp .. 8*grp+7
-  const int kvh = h / (a.num_q_heads / a.num_kv_heads);
+  const int kvh = g_kv;
 
   // ---- this wavefront's queries, held as B operands of S^T = K Q^T ------------------------
   const int wj0 = j0 + wave * kWaveQ;
