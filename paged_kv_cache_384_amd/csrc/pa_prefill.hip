@@ -176,18 +176,27 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
   auto store_tile = [&](int buf, int T0) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bool kin = T0 + ktok < ctx;
+    if (T0 + kTileT > ctx) {  // the tile that holds the context's end (workgroup-uniform)
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const bool kin = T0 + ktok < ctx;
+      const bool v0 = T0 + vtok < ctx;
+      const bool v1 = T0 + vtok + 1 < ctx;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) kr[c] = kin ? kr[c] : zero;
+#pragma unroll
+      for (int it = 0; it < kVTasks; ++it) {
+        vr[it][0] = v0 ? vr[it][0] : zero;
+        vr[it][1] = v1 ? vr[it][1] : zero;
+      }
+    }
     uint8_t* kd = k_s[buf] + ktok * kKRow + grp * 16;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) store16(kd + c * 64, kin ? kr[c] : zero);
-    const bool v0 = T0 + vtok < ctx;
-    const bool v1 = T0 + vtok + 1 < ctx;
+    for (int c = 0; c < kChunks; ++c) store16(kd + c * 64, kr[c]);
     uint8_t* vd = v_s[buf] + vt_slot(vtok) * 2;
 #pragma unroll
     for (int it = 0; it < kVTasks; ++it) {
-      const u32x4 x = v0 ? vr[it][0] : zero;
-      const u32x4 y = v1 ? vr[it][1] : zero;
+      const u32x4 x = vr[it][0];
+      const u32x4 y = vr[it][1];
       const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
       const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
       const int d0 = (vpc + 8 * it) * 8;
@@ -226,6 +235,9 @@ void prefill_kernel(PrefillArgs a) {
     // S^T blocks: st[qb][tb][i] = score of query 16qb+col, token T0 + 16tb + 4grp + i
     f32x4 st[2][4];
     const uint8_t* kb = k_s[buf] + col * kKRow + grp * 16;
+    // matrix-core sections run at raised wave priority, so a wavefront that has its operands
+    // keeps the matrix pipe fed while the SIMD's other wavefront does its softmax arithmetic
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       st[0][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -237,6 +249,7 @@ void prefill_kernel(PrefillArgs a) {
         st[1][tb] = Mfma16x16x32<dt>::run(kf, qf[1][c], st[1][tb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     float mx[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -289,6 +302,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     const uint8_t* vb = v_s[buf] + col * kVtRow + grp * 16;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       lacc[0] = Mfma16x16x32<dt>::run(ones, pb[0][ks], lacc[0]);
@@ -302,6 +316,7 @@ void prefill_kernel(PrefillArgs a) {
         o[0][db] = Mfma16x16x32<dt>::run(vf, pb[0][ks], o[0][db]);
         o[1][db] = Mfma16x16x32<dt>::run(vf, pb[1][ks], o[1][db]);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- walk the tiles ----------------------------------------------------------------------
