@@ -15,7 +15,11 @@ Prints one JSON line. ``value`` is KV bytes read per step / step time (GB/s, who
 ``roofline`` reports the attention kernel alone (HIP events on its stream) against the 8 TB/s
 HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
 
+``prefill`` (default: the GQA prompt workload) times pa_prefill on a prefill batch and reports
+it against the 16-bit matrix-core peak, with its own CPU-oracle sample.
+
     python bench.py [--steps K] [--warmup W] [--config NAME] [--partition P] [--eager]
+                    [--prefill NAMES] [--prefill-only]
 """
 from __future__ import annotations
 
@@ -196,10 +200,54 @@ def swap_rate(cfg, batch, v, stream, reps=5):
     return res
 
 
+def copy_calibration(dev):
+    """Three plain 1 GiB device-to-device copies: the reference for HBM byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 3 x {n} byte device copies", file=sys.stderr)
+
+
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense 16-bit matrix-core peak
 
 
-def prefill_rate(name, steps, warmup, stream):
+def prefill_cpu_baseline(batch, v, budget_s: float):
+    """The CPU oracle's prefill, single-threaded, on query rows of the longest sequence (4 at a
+    time, from its last query down) until ``budget_s`` is spent; flop counted as in the GPU
+    figure (4·d per seen token per query head)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cfg = batch.cfg
+    kw = dict(dtype=cfg.dtype, num_kv_heads=cfg.num_kv_heads, block_size=cfg.block_size,
+              head_dim=cfg.head_dim)
+    host = {k: host_storage(v[k]) for k in ("query", "k_pool", "v_pool")}
+    s = int(batch.query_lens.argmax())
+    n, q = int(batch.context_lens[s]), int(batch.query_lens[s])
+    done_rows, flops = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for hi in range(q, 0, -4):
+            rows = list(range(max(0, hi - 4), hi))
+            oracle.paged_prefill_ref(host["query"], host["k_pool"], host["v_pool"],
+                                     batch.block_tables, batch.query_start, batch.context_lens,
+                                     cfg.scale, seqs=[s], rows={s: rows}, **kw)
+            done_rows += len(rows)
+            flops += sum(4 * cfg.head_dim * cfg.num_q_heads * (n - q + j + 1) for j in rows)
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"the last {done_rows} queries of the longest sequence ({n} tokens), all "
+                      f"{cfg.num_q_heads} query heads, in {dt:.1f} s, numpy float64, 1 thread"}
+
+
+def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0):
     """pa_prefill on a prefill workload: the new tokens' cache write, then the causal attention
     of every new token, K calls each with HIP events on the launch stream. The attention is two
     dense products per key/value tile on the matrix cores, so its roofline is the 16-bit MFMA
@@ -249,6 +297,7 @@ def prefill_rate(name, steps, warmup, stream):
     print(f"[bench] prefill {name}: attention {a_us:.1f} us (p10 {np.percentile(a_list, 10):.1f}, "
           f"p90 {np.percentile(a_list, 90):.1f}) = {tf:.1f} TFLOP/s ({tf / peak:.3f} of peak), "
           f"cache write {w_us:.1f} us", file=sys.stderr, flush=True)
+    cpu = prefill_cpu_baseline(batch, v, cpu_budget) if cpu_budget > 0 else None
     return {"workload": name, "description": cfg.description, "dtype": cfg.dtype,
             "new_tokens": new_tokens, "context_tokens": int(batch.context_lens.sum()),
             "attention_us": round(a_us, 2), "cache_write_us": round(w_us, 2),
@@ -256,7 +305,8 @@ def prefill_rate(name, steps, warmup, stream):
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
                          "kernel": "prefill_kernel", "avg_us": round(a_us, 2),
-                         "flops_per_launch": flops}}
+                         "flops_per_launch": flops},
+            "cpu_baseline": cpu}
 
 
 def main():
@@ -281,9 +331,9 @@ def main():
     ap.add_argument("--swap", action="store_true",
                     help="also time swapping every block of half the sequences out to pinned "
                          "host memory and back (pa_swap_blocks)")
-    ap.add_argument("--prefill", default="",
+    ap.add_argument("--prefill", default="prefill_bf16",
                     help="comma-separated prefill workloads to time as well (pa_prefill), e.g. "
-                         "prefill_bf16,chunked_fp16")
+                         "prefill_bf16,chunked_fp16; empty for none")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the --prefill workloads and print their JSON")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -307,7 +357,10 @@ def main():
     prefill_names = [n for n in args.prefill.split(",") if n]
     if args.prefill_only:
         stream = torch.cuda.current_stream(dev)
-        res = [prefill_rate(n, args.steps, args.warmup, stream) for n in prefill_names]
+        budget = 0.0 if args.no_cpu_baseline else 5.0
+        res = [prefill_rate(n, args.steps, args.warmup, stream, budget) for n in prefill_names]
+        if args.copy_calibration:
+            copy_calibration(dev)
         print(json.dumps({"prefill": res}), flush=True)
         return
     cfg = wl.CONFIGS[args.config]
@@ -408,14 +461,7 @@ def main():
               file=sys.stderr, flush=True)
 
     if args.copy_calibration:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        a.fill_(1)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: 3 x {n} byte device copies", file=sys.stderr)
+        copy_calibration(dev)
 
     achieved = kv_bytes / (attn_avg * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -432,7 +478,8 @@ def main():
     if args.paging_overhead:
         paging = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream)
 
-    prefill = [prefill_rate(n, args.steps, args.warmup, stream) for n in prefill_names]
+    budget = 0.0 if args.no_cpu_baseline else 5.0
+    prefill = [prefill_rate(n, args.steps, args.warmup, stream, budget) for n in prefill_names]
 
     cpu = None
     if not args.no_cpu_baseline:
