@@ -15,22 +15,24 @@
 // head); each wavefront owns 32 of them as two 16-query MFMA columns. The workgroup walks the
 // sequence's tokens in tiles of 64, from token 0 to the last position its queries can see:
 //   * the tile's key rows and value rows are gathered through the block table into LDS (double
-//     buffered, the next tile's global loads in flight while the current one is computed). Key
-//     rows keep their order (a padded row per token); value rows are transposed into dim rows
-//     (a padded row per head dimension), in the token order the P operand needs (below);
+//     buffered, the next tile's global loads in flight while the current one is computed), one
+//     288-byte row per token for each (288 = 8 words mod 64 banks: the operand reads below are
+//     free of bank conflicts at that stride on gfx950, measured);
 //   * each wavefront forms S^T = K Q^T: A = 16 tokens x 32 dims read from LDS, B = its queries
 //     held in registers since the start. Lane l gets query l%16 and tokens 4(l/16)..4(l/16)+3 of
 //     each 16-token block;
 //   * online softmax per query (column), in the base-2 domain: causal mask on tiles that reach
-//     past a query's position, running maximum shared by the four lanes of a column, rescaling of
-//     the output only when the maximum grows by more than a slack of 2^8 (the final division by
-//     the running sum makes the result exact either way). The running sum is one more matrix
-//     product (all-ones A times the packed weights), so it sums exactly the 16-bit weights that
-//     multiply the values;
-//   * O^T += V^T P^T: A = 16 dims x 32 tokens from the transposed value rows, B = the
-//     probabilities, packed to 16 bits straight from the S^T registers. Lane l's eight k values
-//     are tokens {4(l/16)+i, 16+4(l/16)+i} (i < 4) of a 32-token step; the value rows are stored
-//     in that order, so P never moves between lanes.
+//     past a query's position, running maximum shared by the four lanes of a column (permlane
+//     swaps), rescaling of the output only when the maximum grows by more than a slack of 2^8
+//     (the final division by the running sum makes the result exact either way). The running
+//     sum is one more matrix product (all-ones A times the packed weights), so it sums exactly
+//     the 16-bit weights that multiply the values;
+//   * O^T += V^T P^T: B = the probabilities, packed to 16 bits straight from the S^T registers;
+//     lane l's eight k values are tokens {4(l/16)+i, 16+4(l/16)+i} (i < 4) of a 32-token step.
+//     A = 16 dims x those 32 tokens, read from the token-major value rows by the transposing
+//     LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives element b of
+//     the 4-element chunk that lane 4k+a addresses, for k = 0..3, so lanes addressing (token k,
+//     dims 4a..4a+3) hand every lane 4 tokens of its own dim.
 // Tokens at or past the context length are zero in LDS (their table entries are never read), so
 // slots past the end of the last block do not matter, whatever they hold.
 #include <type_traits>
@@ -51,6 +53,27 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 static_assert(kPrefillThreads / 64 * kWaveQ == kTileQ, "four wavefronts of 32 queries");
 static_assert(kTileT == 64, "the token permutation below covers two 32-token MFMA steps");
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 from an LDS address: 4 16-bit elements, transposed across each group of 16
+// lanes (see the file comment).
+__device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Maximum over lanes l, l^16, l^32, l^48 (the four rows of 16 lanes), in every lane: a
+// v_permlane16_swap and a v_permlane32_swap of the value with itself give each lane its partner
+// in the other half of the row pair / wave half.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f32_bits(x), f32_bits(x), false, false);
+  x = fmaxf(bits_f32(a[0]), bits_f32(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return fmaxf(bits_f32(b[0]), bits_f32(b[1]));
+}
+
 // Two fp32 values rounded (nearest even) to the 16-bit type and packed, low half first: one
 // v_cvt_pk_{f16,bf16}_f32 on gfx950.
 template <DType dt> struct Pack2;
@@ -67,15 +90,6 @@ template <> struct Pack2<DType::BF16> {
   }
 };
 
-// Position of token t (0..63) of a tile in a transposed value row: the 32-token MFMA step
-// ks = t/32 takes, in lane group r = (t%16)/4, tokens 4r..4r+3 of the step's first 16 and then
-// 16+4r..16+4r+3, so a lane's 16-byte operand is eight adjacent 16-bit slots.
-__device__ __forceinline__ int vt_slot(int t) {
-  const int ks = t >> 5;
-  const int u = t & 31;
-  return ks * 32 + ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
-}
-
 }  // namespace
 
 // Two workgroups per CU (eight wavefronts, two per SIMD): registers are capped at 256 per lane
@@ -87,11 +101,11 @@ void prefill_kernel(PrefillArgs a) {
   static_assert(G::kEsz == 2, "matrix-core prefill takes 16-bit elements");
   constexpr int kChunks = D / 32;          // 64-byte chunks (32 dims) per key row
   constexpr int kDBlocks = D / 16;         // 16-dim output blocks
-  constexpr int kKRow = D * 2 + 16;        // LDS key row: one token, padded by 16 bytes
-  constexpr int kVtRow = kTileT * 2 + 16;  // LDS value row: one dim of 64 tokens, padded
-  constexpr int kVTasks = D / 64;          // (token pair, 16-byte piece) tasks per thread
-  __shared__ __align__(16) uint8_t k_s[2][kTileT * kKRow];
-  __shared__ __align__(16) uint8_t v_s[2][D * kVtRow];
+  constexpr int kRow = 288;                // LDS row of one token (keys or values), padded
+  constexpr int kVPieces = D / 32;         // 16-byte value pieces per lane per tile
+  static_assert(D * 2 <= kRow, "a token's head vector fits one LDS row");
+  __shared__ __align__(16) uint8_t k_s[2][kTileT * kRow];
+  __shared__ __align__(16) uint8_t v_s[2][kTileT * kRow];
 
   // ---- which queries ---------------------------------------------------------------------
   // A unit is (query tile qt, sequence, KV head); its G query heads read the same key/value
@@ -146,11 +160,11 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- gathering a tile: the loads each thread issues --------------------------------------
-  // keys: token 16*wave + col of the tile, 16-byte piece grp of each 64-byte chunk
+  // Lane (col, grp) of wavefront w loads token 16w + col of the tile: of its key, 16-byte piece
+  // grp of each 64-byte chunk (a wave load covers 16 tokens' chunk c: one contiguous 1 KiB key
+  // chunk row at B = 16); of its value, pieces grp + 4i (a wave load covers 64 bytes of each
+  // of 16 token rows).
   const int ktok = wave * 16 + col;
-  // values: tokens vtok and vtok + 1 (same block: B is even), 16-byte pieces vpc + 8*it
-  const int vtok = 2 * (tid & 31);
-  const int vpc = tid >> 5;
   const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
   // the table entry of token t (clamped to the context, so entries past it are never read), and
   // the byte offset of (block b, this KV head) with b clamped into the pool
@@ -163,52 +177,29 @@ void prefill_kernel(PrefillArgs a) {
     return (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * G::kTileBytes;
   };
   u32x4 kr[kChunks];
-  u32x4 vr[kVTasks][2];
-  auto load_tile = [&](int64_t kt, int64_t vt) {
-    const uint8_t* kp = a.k_pool + kt + (ktok % B) * 64 + grp * 16;
+  u32x4 vr[kVPieces];
+  auto load_tile = [&](int64_t tile) {
+    const uint8_t* kp = a.k_pool + tile + (ktok % B) * 64 + grp * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) kr[c] = load16(kp + c * G::kChunkRowBytes);
-    const uint8_t* vp = a.v_pool + vt + (vtok % B) * G::kRowBytes + vpc * 16;
+    const uint8_t* vp = a.v_pool + tile + (ktok % B) * G::kRowBytes + grp * 16;
 #pragma unroll
-    for (int it = 0; it < kVTasks; ++it) {
-      vr[it][0] = load16(vp + it * 128);
-      vr[it][1] = load16(vp + G::kRowBytes + it * 128);
-    }
+    for (int i = 0; i < kVPieces; ++i) vr[i] = load16(vp + i * 64);
   };
   auto store_tile = [&](int buf, int T0) {
-    if (T0 + kTileT > ctx) {  // the tile that holds the context's end (workgroup-uniform)
+    if (T0 + kTileT > ctx && T0 + ktok >= ctx) {  // past the context's end: zeros
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      const bool kin = T0 + ktok < ctx;
-      const bool v0 = T0 + vtok < ctx;
-      const bool v1 = T0 + vtok + 1 < ctx;
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) kr[c] = kin ? kr[c] : zero;
+      for (int c = 0; c < kChunks; ++c) kr[c] = zero;
 #pragma unroll
-      for (int it = 0; it < kVTasks; ++it) {
-        vr[it][0] = v0 ? vr[it][0] : zero;
-        vr[it][1] = v1 ? vr[it][1] : zero;
-      }
+      for (int i = 0; i < kVPieces; ++i) vr[i] = zero;
     }
-    uint8_t* kd = k_s[buf] + ktok * kKRow + grp * 16;
+    uint8_t* kd = k_s[buf] + ktok * kRow + grp * 16;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) store16(kd + c * 64, kr[c]);
-    uint8_t* vd = v_s[buf] + vt_slot(vtok) * 2;
+    uint8_t* vd = v_s[buf] + ktok * kRow + grp * 16;
 #pragma unroll
-    for (int it = 0; it < kVTasks; ++it) {
-      const u32x4 x = vr[it][0];
-      const u32x4 y = vr[it][1];
-      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-      const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
-      const int d0 = (vpc + 8 * it) * 8;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // dims d0+2k and d0+2k+1 of the two tokens, as (token vtok, token vtok+1) pairs
-        *reinterpret_cast<uint32_t*>(vd + (d0 + 2 * k) * kVtRow) =
-            (xw[k] & 0xffffu) | (yw[k] << 16);
-        *reinterpret_cast<uint32_t*>(vd + (d0 + 2 * k + 1) * kVtRow) =
-            (xw[k] >> 16) | (yw[k] & 0xffff0000u);
-      }
-    }
+    for (int i = 0; i < kVPieces; ++i) store16(vd + i * 64, vr[i]);
   };
 
   // ---- running softmax state and output (O^T blocks: dims 16*db + 4*grp + i, query col) ---
@@ -234,7 +225,7 @@ void prefill_kernel(PrefillArgs a) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     // S^T blocks: st[qb][tb][i] = score of query 16qb+col, token T0 + 16tb + 4grp + i
     f32x4 st[2][4];
-    const uint8_t* kb = k_s[buf] + col * kKRow + grp * 16;
+    const uint8_t* kb = k_s[buf] + col * kRow + grp * 16;
     // matrix-core sections run at raised wave priority, so a wavefront that has its operands
     // keeps the matrix pipe fed while the SIMD's other wavefront does its softmax arithmetic
     __builtin_amdgcn_s_setprio(1);
@@ -244,7 +235,7 @@ void prefill_kernel(PrefillArgs a) {
       st[1][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
-        const u32x4 kf = load16(kb + tb * 16 * kKRow + c * 64);
+        const u32x4 kf = load16(kb + tb * 16 * kRow + c * 64);
         st[0][tb] = Mfma16x16x32<dt>::run(kf, qf[0][c], st[0][tb]);
         st[1][tb] = Mfma16x16x32<dt>::run(kf, qf[1][c], st[1][tb]);
       }
@@ -266,8 +257,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int tb = 1; tb < 4; ++tb)
         mq = fmaxf(mq, fmaxf(fmaxf(st[qb][tb][0], st[qb][tb][1]),
                              fmaxf(st[qb][tb][2], st[qb][tb][3])));
-      mq = fmaxf(mq, __shfl_xor(mq, 16, 64));
-      mq = fmaxf(mq, __shfl_xor(mq, 32, 64));
+      mq = max_over_rows(mq);
       mx[qb] = mq * a.scale_log2;
     }
     if (__builtin_amdgcn_ballot_w64(mx[0] > m[0] + thresh || mx[1] > m[1] + thresh) != 0) {
@@ -301,7 +291,9 @@ void prefill_kernel(PrefillArgs a) {
         pb[qb][ks].w = Pack2<dt>::run(pr[2 * ks + 1][2], pr[2 * ks + 1][3]);
       }
     }
-    const uint8_t* vb = v_s[buf] + col * kVtRow + grp * 16;
+    // transposing reads: this lane addresses token 4grp + col/4 (+16) of the step, dims
+    // 16db + 4(col%4) .. +3, and receives dim 16db + col of tokens 4grp .. 4grp+3 (16+...)
+    const uint8_t* vb = v_s[buf] + (4 * grp + (col >> 2)) * kRow + 8 * (col & 3);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -312,7 +304,9 @@ void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        const u32x4 vf = load16(vb + db * 16 * kVtRow + ks * 64);
+        const u32x2 lo = read_tr16(vb + ks * 32 * kRow + db * 32);
+        const u32x2 hi = read_tr16(vb + (ks * 32 + 16) * kRow + db * 32);
+        const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
         o[0][db] = Mfma16x16x32<dt>::run(vf, pb[0][ks], o[0][db]);
         o[1][db] = Mfma16x16x32<dt>::run(vf, pb[1][ks], o[1][db]);
       }
@@ -323,7 +317,7 @@ void prefill_kernel(PrefillArgs a) {
   // The block ids of tile i+2 are loaded while tile i is computed and turned into addresses only
   // at step i+1, when the tile's own loads are issued, so no step waits on a table read.
   if (n_steps > 0) {
-    load_tile(tile_of(table_block(ktok)), tile_of(table_block(vtok)));
+    load_tile(tile_of(table_block(ktok)));
     // Every load so far (the queries and tile 0) completes here. Without this explicit wait the
     // compiler's wait-count analysis, which cannot see that the query registers are complete
     // once the first tile is, waits for every in-flight tile load before each step's first
@@ -331,7 +325,6 @@ void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     store_tile(0, 0);
     int kb_next = table_block(kTileT + ktok);
-    int vb_next = table_block(kTileT + vtok);
     __syncthreads();
     const int wp_lo = base_p + wj0;  // every column of the wave sees tokens 0..wp_lo
     const int wp_hi = base_p + wj1;  // no column sees a token past wp_hi
@@ -339,9 +332,8 @@ void prefill_kernel(PrefillArgs a) {
       const int T0 = step * kTileT;
       const bool more = step + 1 < n_steps;
       if (more) {
-        load_tile(tile_of(kb_next), tile_of(vb_next));
+        load_tile(tile_of(kb_next));
         kb_next = table_block(T0 + 2 * kTileT + ktok);
-        vb_next = table_block(T0 + 2 * kTileT + vtok);
       }
       if (w_active && T0 <= wp_hi) {
         if (T0 + kTileT - 1 > wp_lo) compute(step & 1, T0, std::true_type{});
