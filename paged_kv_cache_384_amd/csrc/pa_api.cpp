@@ -278,9 +278,11 @@ pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* 
     return PA_ERR_SHAPE;
   const int64_t tiles = (static_cast<int64_t>(max_query_len) + pa::kPrefillTileQueries - 1) /
                         pa::kPrefillTileQueries;
-  const int64_t units = tiles * num_seqs * c->num_kv_heads;
   const int64_t group = num_q_heads / c->num_kv_heads;
-  const int64_t wgs = (units + 7) / 8 * 8 * group;
+  const bool seq_major = tiles <= pa::kPrefillSeqMajorTiles;
+  const int64_t units = (seq_major ? 1 : tiles) * num_seqs * c->num_kv_heads;
+  const int64_t unit_wgs = (seq_major ? tiles : 1) * group;
+  const int64_t wgs = (units + 7) / 8 * 8 * unit_wgs;
   if (wgs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
   if (wgs == 0) return PA_OK;
   if (!key_cache || !value_cache || !out || !query || !block_tables || !query_start ||
@@ -307,7 +309,9 @@ pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* 
   a.max_ctx = max_context_len;
   a.group = static_cast<int32_t>(group);
   a.q_tiles = static_cast<int32_t>(tiles);
+  a.seq_major = seq_major ? 1 : 0;
   a.num_units = static_cast<int32_t>(units);
+  a.unit_wgs = static_cast<int32_t>(unit_wgs);
   a.num_wgs = static_cast<int32_t>(wgs);
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   if (pa::launch_prefill(static_cast<DType>(c->dtype), c->head_dim, c->block_size, a,

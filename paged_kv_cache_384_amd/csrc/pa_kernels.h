@@ -92,10 +92,15 @@ struct PrefillArgs {
   int32_t max_ctx;
   int32_t group;        // query heads per KV head
   int32_t q_tiles;      // ceil(max_query_len / kPrefillTileQueries)
-  int32_t num_units;    // q_tiles * num_seqs * num_kv_heads: (query tile, sequence, KV head)
-  int32_t num_wgs;      // num_units rounded up to a multiple of 8 (the XCDs), times group
+  int32_t seq_major;    // 1: units are (sequence, KV head); 0: (query tile, sequence, KV head)
+  int32_t num_units;    // units of workgroups that read the same key/value tiles
+  int32_t unit_wgs;     // workgroups per unit: group, times q_tiles when seq_major
+  int32_t num_wgs;      // num_units rounded up to a multiple of 8 (the XCDs), times unit_wgs
   float scale_log2;     // scale * log2(e)
 };
+
+// Units are sequence-major when every sequence has at most this many query tiles.
+constexpr int kPrefillSeqMajorTiles = 4;
 
 // Each launcher returns the hipError_t of its launch (hipSuccess when nothing was launched).
 hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,

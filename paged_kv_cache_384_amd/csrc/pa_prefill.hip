@@ -108,19 +108,33 @@ void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) uint8_t v_s[2][kTileT * kRow];
 
   // ---- which queries ---------------------------------------------------------------------
-  // A unit is (query tile qt, sequence, KV head); its G query heads read the same key/value
-  // tiles. The hardware deals workgroups round-robin over the 8 XCDs (blockIdx % 8), each with
-  // its own L2: unit u goes to XCD u % 8, where its G heads run as consecutive workgroups and
-  // share that L2. Units are numbered from the highest query tile down, so the longest-running
-  // workgroups (the latest queries of a prompt see the most tokens) start first on every XCD.
+  // Workgroups come in units whose members read the same key/value tiles and run as
+  // consecutive workgroups on one XCD, sharing its L2: the hardware deals workgroups
+  // round-robin over the 8 XCDs (blockIdx % 8), so unit u goes to XCD u % 8.
+  //   tile-major (many query tiles per sequence: prompts): a unit is (query tile, sequence, KV
+  //     head) and holds the G query heads; units are numbered from the highest query tile down,
+  //     so the longest-running workgroups (the latest queries of a prompt see the most tokens)
+  //     start first on every XCD;
+  //   sequence-major (a few query tiles per sequence: chunks on top of a long context, whose
+  //     tiles cost about the same): a unit is (sequence, KV head) and holds all its query tiles
+  //     and query heads, which then read the sequence's key/value tiles from the L2 together
+  //     instead of from HBM once per tile.
   const int group = a.group;
   const int k8 = static_cast<int>(blockIdx.x >> 3);
-  const int u = (k8 / group) * 8 + static_cast<int>(blockIdx.x & 7);
+  const int u = (k8 / a.unit_wgs) * 8 + static_cast<int>(blockIdx.x & 7);
   if (u >= a.num_units) return;
-  const int h_in = k8 % group;
-  const int g_kv = u % a.num_kv_heads;
-  const int s = (u / a.num_kv_heads) % a.num_seqs;
-  const int qt = a.q_tiles - 1 - u / (a.num_kv_heads * a.num_seqs);
+  const int within = k8 % a.unit_wgs;
+  const int h_in = within % group;
+  int g_kv, s, qt;
+  if (a.seq_major) {
+    g_kv = u % a.num_kv_heads;
+    s = u / a.num_kv_heads;
+    qt = a.q_tiles - 1 - within / group;
+  } else {
+    g_kv = u % a.num_kv_heads;
+    s = (u / a.num_kv_heads) % a.num_seqs;
+    qt = a.q_tiles - 1 - u / (a.num_kv_heads * a.num_seqs);
+  }
   const int h = g_kv * group + h_in;
   const int q0 = a.query_start[s];
   int n_q = a.query_start[s + 1] - q0;
