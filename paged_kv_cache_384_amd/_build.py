@@ -20,6 +20,11 @@ SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_attention_b8.hip", "pa_attention_b1
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+# Per-source additions. The prefill kernel takes maxima of MFMA results; in IEEE mode each
+# fmaxf operand first gets a quieting v_max_f32 x, x (64 extra VALU per key/value tile), which
+# -fno-honor-nans drops. The kernel never relies on NaN propagation: slots past a context are
+# zeroed by position before they reach a product.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -34,7 +39,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [hipcc(), *FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, *lang, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -70,3 +70,41 @@ def test_graph_replay_matches_eager(name, over):
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
     assert np.isfinite(eager.float().cpu().numpy()).all()
+
+
+def test_prefill_graph_replay_matches_eager():
+    """A prefill step (cache write of every new token, then pa_prefill) captured once and
+    replayed with eager work in between reproduces the eager step bit for bit; the eager step
+    matches the oracle (the same inputs as the small prefill parity case)."""
+    from _gpu_cases import Prepared, run_prefill
+    cfg = wl.DecodeConfig("graph_prefill", "bf16", num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, block_size=16, ctx=("uniform", 100, 600),
+                          new_tokens=("uniform", 1, 300), seed=21)
+    P = Prepared(cfg, poison=False)
+    log("[graph] prefill: eager step against the oracle")
+    run_prefill(cfg, prepared=P)
+    b = P.batch
+    out = torch.empty_like(P.q_d)
+
+    def step(o):
+        pa.pa_reshape_and_cache(P.kp_d, P.vp_d, P.key_d, P.val_d, P.bt_d, P.seq_d, P.pos_d)
+        pa.pa_prefill(o, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d, P.ctx_d, cfg.scale,
+                      b.max_query_len, b.max_context_len)
+
+    step(out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    other = torch.empty_like(out)
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"[graph] prefill replay {r}")
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} output"
+        step(other)
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
