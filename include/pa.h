@@ -127,7 +127,9 @@ PA_API pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, v
 
 /*
  * pa_decode_workspace_bytes — bytes of device workspace pa_decode needs for these sizes.
- * partition_size 0 means the library's choice (the same one pa_decode makes). Returns 0 when
+ * partition_size 0 means the library's choice (the same one pa_decode makes: 512 tokens for
+ * workgroups of one query head, 1024 when an even group size lets a workgroup serve 2 or 4
+ * query heads). Returns 0 when
  * no workspace is needed (every context fits one partition) and (size_t)-1 for invalid sizes.
  */
 PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,

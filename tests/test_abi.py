@@ -134,16 +134,21 @@ def test_contiguous_twin_validation(L):
 def test_workspace_bytes(L):
     # block sizes 8 and 32: the default partition rounds a short context up to whole
     # 16-token groups and whole blocks
-    for b, ctx, parts in ((8, 100, 1), (32, 100, 1), (32, 4096, 8)):
+    # (4 query heads per KV head: default partitions of 1024 tokens)
+    for b, ctx, parts in ((8, 100, 1), (32, 100, 1), (32, 4096, 4)):
         n = L.pa_decode_workspace_bytes(ctypes.byref(desc(dtype=2, hkv=8, d=128, b=b)), 4, 32,
                                         ctx, 0)
         assert n == (0 if parts == 1 else 4 * 32 * parts * 130 * 4), (b, ctx)
     d = desc(dtype=2, hkv=8, d=128)
     # longest context fits the default partition: no workspace
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 512, 0) == 0
-    # default 512-token partitions: ceil(4096 / 512) = 8 states of (d + 2) floats per (seq, head)
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 4096, 0) == 256 * 32 * 8 * 130 * 4
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 1024, 0) == 0
+    # workgroups of 4 query heads: ceil(4096 / 1024) = 4 states of (d + 2) floats per (seq, head)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 256, 32, 4096, 0) == 256 * 32 * 4 * 130 * 4
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 8, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    # single-head workgroups (MHA): 512-token default partitions
+    m = desc(dtype=1, hkv=40, d=128)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(m), 64, 40, 512, 0) == 0
+    assert L.pa_decode_workspace_bytes(ctypes.byref(m), 64, 40, 2048, 0) == 64 * 40 * 4 * 130 * 4
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 33, 100, 0) == ctypes.c_size_t(-1).value
 
 
