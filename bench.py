@@ -13,7 +13,8 @@ skips the graph pass and reports the eager step time instead).
 
 Prints one JSON line. ``value`` is KV bytes read per step / step time (GB/s, whole step);
 ``roofline`` reports the attention kernel alone (HIP events on its stream) against the 8 TB/s
-HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
+HBM peak; ``hbm_copy_gbps`` is a plain 1 GiB device copy on the same GPU (``frac_of_copy`` =
+value / that); ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
 
 ``prefill`` (default: the GQA prompt workload) times pa_prefill on a prefill batch and reports
 it against the 16-bit matrix-core peak, with its own CPU-oracle sample.
@@ -198,6 +199,29 @@ def swap_rate(cfg, batch, v, stream, reps=5):
     print(f"[bench] swap {n} blocks ({nbytes / 1e6:.1f} MB each way): out {res['out_gbps']} GB/s, "
           f"in {res['in_gbps']} GB/s", file=sys.stderr, flush=True)
     return res
+
+
+def copy_bandwidth(dev, reps=5):
+    """A plain 1 GiB device-to-device copy (read + written bytes / time, HIP events): the
+    achievable HBM bandwidth the attention kernel is also compared against."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * n / s / 1e9, 1)
 
 
 def copy_calibration(dev):
@@ -486,6 +510,7 @@ def main():
         host = {name: host_storage(sets[0][name]) for name in ("query", "k_pool", "v_pool")}
         cpu = cpu_baseline(batch, host, args.cpu_budget)
 
+    copy_gbps = copy_bandwidth(dev)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     line = {
         "metric": "pa_decode KV-read HBM GB/s (fraction of MI355X peak) + decode tokens/s",
@@ -509,6 +534,10 @@ def main():
                    "copy_pairs": int(n_pairs), "shared_blocks": bool(shared)},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
+        "tokens_per_s_attention_only": round(
+            cfg.num_seqs / ((attn_avg + float(np.mean(red_us))) * 1e-6), 1),
+        "hbm_copy_gbps": copy_gbps,
+        "frac_of_copy": round(value / copy_gbps, 4),
         "launch": "eager" if args.eager else "hip_graph",
         "ms_per_step_eager": round(ms_step_eager, 5),
         "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),
