@@ -73,6 +73,23 @@ def test_prefill_empty_sequences_and_zero_len():
     assert torch.isnan(out.float()).all()
 
 
+def test_prefill_long_context_chunks():
+    """Chunks on top of 16K-20K-token contexts (several hundred key/value tiles per workgroup,
+    block tables of hundreds of entries), bf16 GQA at B = 32; sampled queries of every sequence,
+    first and last included."""
+    cfg = small("long_chunk_bf16", "bf16", 3, 8, 2, 128, 32, ("uniform", 16000, 20000),
+                ("uniform", 200, 300), 19)
+    P = Prepared(cfg, device_values=True)
+    ql = P.batch.query_lens
+    rng = np.random.default_rng(7)
+    rows = {s: sorted({0, int(ql[s]) - 1} | set(rng.integers(0, ql[s], 6).tolist()))
+            for s in range(cfg.num_seqs)}
+    log(f"[prefill] long chunks ctx={P.batch.context_lens.tolist()} q={ql.tolist()}")
+    r = run_prefill(cfg, rows=rows, prepared=P)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} beyond output rounding "
+        f"{r['excess_err']:.3g}")
+
+
 @pytest.mark.parametrize("name", ["prefill_bf16", "chunked_fp16"])
 @pytest.mark.timeout(900)
 def test_prefill_full_size(name):
