@@ -16,8 +16,8 @@
 // sequence's tokens in tiles of 64, from token 0 to the last position its queries can see:
 //   * the tile's key rows and value rows are gathered through the block table into LDS (double
 //     buffered, the next tile's global loads in flight while the current one is computed), one
-//     288-byte row per token for each (288 = 8 words mod 64 banks: the operand reads below are
-//     free of bank conflicts at that stride on gfx950, measured);
+//     288-byte row per token for each (72 dwords, 8 more than a multiple of the 64 banks: the
+//     operand reads below are free of bank conflicts at that stride on gfx950, measured);
 //   * each wavefront forms S^T = K Q^T: A = 16 tokens x 32 dims read from LDS, B = its queries
 //     held in registers since the start. Lane l gets query l%16 and tokens 4(l/16)..4(l/16)+3 of
 //     each 16-token block;
