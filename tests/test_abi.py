@@ -263,3 +263,27 @@ def test_prefill_validation(L):
     assert pf(mql=0, ptrs=none) == OK
     assert pf(desc(dtype=2, d=64, b=8), S=0, max_ctx=64, ptrs=none) == OK
     assert pf(desc(dtype=2, d=64, b=8), S=0, max_ctx=65, ptrs=none) == SHAPE
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    """The Python binding checks placement and shapes before any call reaches the library."""
+    import torch
+    if not os.path.exists(pa.library_path):
+        pytest.skip("libpa.so not built")
+    q = torch.zeros(10, 4, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(8, 2, 16 * 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    qs = torch.tensor([0, 4, 10], dtype=torch.int32)
+    ctx = torch.tensor([4, 6], dtype=torch.int32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pa.pa_prefill(torch.empty_like(q), q, pool, pool, bt, qs, ctx, 0.1, 6, 64)
+    with pytest.raises(ValueError, match="out must match"):
+        pa.pa_prefill(torch.empty(9, 4, 128, dtype=torch.bfloat16), q, pool, pool, bt, qs, ctx,
+                      0.1, 6, 64)
+    with pytest.raises(ValueError, match="query_start"):
+        pa.pa_prefill(torch.empty_like(q), q, pool, pool, bt, qs[:2], ctx, 0.1, 6, 64)
+    with pytest.raises(ValueError, match="pools must be"):
+        pa.pa_prefill(torch.empty_like(q), q, pool[:, :, :100], pool, bt, qs, ctx, 0.1, 6, 64)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pa.pa_decode(torch.empty(2, 4, 128, dtype=torch.bfloat16),
+                     torch.zeros(2, 4, 128, dtype=torch.bfloat16), pool, pool, bt, ctx, 0.1, 64)
