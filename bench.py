@@ -271,17 +271,18 @@ def prefill_cpu_baseline(batch, v, budget_s: float):
                       f"{cfg.num_q_heads} query heads, in {dt:.1f} s, numpy float64, 1 thread"}
 
 
-def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0):
+def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0, **overrides):
     """pa_prefill on a prefill workload: the new tokens' cache write, then the causal attention
     of every new token, K calls each with HIP events on the launch stream. The attention is two
     dense products per key/value tile on the matrix cores, so its roofline is the 16-bit MFMA
-    peak, with the flops counted from the causal definition (no masked or padded work)."""
+    peak, with the flops counted from the causal definition (no masked or padded work).
+    ``overrides`` replace workload fields (block_size, placement)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_384_amd as pa
     from paged_kv_cache_384_amd import workloads as wl
-    cfg = wl.PREFILL_CONFIGS[name]
+    cfg = wl.config(name, **overrides)
     batch = wl.build_batch(cfg)
     dev = torch.device("cuda:0")
     v = wl.make_values(batch, device=dev, seed=0, poison_nan=False)
@@ -323,6 +324,7 @@ def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0):
           f"cache write {w_us:.1f} us", file=sys.stderr, flush=True)
     cpu = prefill_cpu_baseline(batch, v, cpu_budget) if cpu_budget > 0 else None
     return {"workload": name, "description": cfg.description, "dtype": cfg.dtype,
+            "block_size": cfg.block_size, "placement": cfg.placement,
             "new_tokens": new_tokens, "context_tokens": int(batch.context_lens.sum()),
             "attention_us": round(a_us, 2), "cache_write_us": round(w_us, 2),
             "tokens_per_s": round(new_tokens / ((a_us + w_us) * 1e-6), 1),
@@ -359,7 +361,10 @@ def main():
                     help="comma-separated prefill workloads to time as well (pa_prefill), e.g. "
                          "prefill_bf16,chunked_fp16; empty for none")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the --prefill workloads and print their JSON")
+                    help="time only the --prefill workloads and print their JSON (--block-size "
+                         "and --placement then apply to them)")
+    ap.add_argument("--placement", default="", choices=["", "shuffled", "contiguous"],
+                    help="with --prefill-only: physical block placement of the prefill batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -382,7 +387,13 @@ def main():
     if args.prefill_only:
         stream = torch.cuda.current_stream(dev)
         budget = 0.0 if args.no_cpu_baseline else 5.0
-        res = [prefill_rate(n, args.steps, args.warmup, stream, budget) for n in prefill_names]
+        over = {}
+        if args.block_size:
+            over.update(block_size=args.block_size, num_blocks=0)
+        if args.placement:
+            over.update(placement=args.placement)
+        res = [prefill_rate(n, args.steps, args.warmup, stream, budget, **over)
+               for n in prefill_names]
         if args.copy_calibration:
             copy_calibration(dev)
         print(json.dumps({"prefill": res}), flush=True)
