@@ -37,6 +37,10 @@ CASES = [
     small("chunk_bf16_d64_b32", "bf16", 4, 6, 3, 64, 32, ("uniform", 200, 500), ("uniform", 60, 200), 15),
     # one query per sequence: the decode case
     small("one_f16", "f16", 6, 8, 8, 128, 16, ("uniform", 1, 400), ("one",), 16),
+    # three query heads per KV head; at most 4 query tiles per sequence (sequence-major units)
+    # and more (tile-major units)
+    small("g3_seq_major_f16", "f16", 3, 6, 2, 128, 16, ("fixed", (70, 200, 129)), ("all",), 20),
+    small("g3_tile_major_bf16", "bf16", 3, 6, 2, 64, 16, ("fixed", (700, 300, 650)), ("all",), 22),
 ]
 
 
