@@ -247,7 +247,9 @@ PA_API pa_status pa_decode_contiguous(const pa_cache_desc* c, const void* key_ca
  * failed launch gives PA_ERR_LAUNCH. num_seqs = 0 or max_query_len = 0 returns PA_OK.
  * Caller contract (not checked on the device beyond clamping): q_len <= n; a query whose
  * position would be negative (q_len > n) gets a zero row. A block id outside [0, NB) is clamped
- * into range (no fault, but the result is then meaningless).
+ * into range (no fault, but the result is then meaningless). NaN in a query or in a key/value
+ * inside a context gives an unspecified output row (the kernel does not propagate NaN); slots
+ * past a context are never used, whatever they hold.
  */
 PA_API pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* value_cache,
                             void* out, const void* query, const int32_t* block_tables,
