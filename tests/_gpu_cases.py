@@ -184,13 +184,15 @@ def run_step(cfg, *, partition_size=0, sample=None, device_values=False, poison=
 
 
 def run_prefill(cfg, *, rows=None, device_values=False, poison=True, check_pools=True,
-                value_seed=0, max_query_len=None, prepared=None):
+                value_seed=0, max_query_len=None, max_context_len=None, prepared=None):
     """One prefill step on the GPU (cache writes of every new token, then pa_prefill) checked
     against the oracle.
 
     rows: None = every query row through the oracle; else a dict seq -> list of query indices j.
     max_query_len: passed to pa_prefill (default: the batch's largest q_len); queries at or past
     it must be left untouched (NaN in the output buffer).
+    max_context_len: passed to pa_prefill (default: the batch's longest context); longer
+    contexts are truncated to it, on both sides.
     Returns a dict of measured errors.
     """
     t0 = time.time()
@@ -200,9 +202,9 @@ def run_prefill(cfg, *, rows=None, device_values=False, poison=True, check_pools
     res = {"prep_s": time.time() - t0}
     P.write_cache(check_pools)
     mql = batch.max_query_len if max_query_len is None else max_query_len
+    mcl = batch.max_context_len if max_context_len is None else max_context_len
     out_d = torch.full_like(P.q_d, float("nan"))
-    pa.pa_prefill(out_d, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d, P.ctx_d, cfg.scale, mql,
-                  batch.max_context_len)
+    pa.pa_prefill(out_d, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d, P.ctx_d, cfg.scale, mql, mcl)
     torch.cuda.synchronize()
     out = to_storage(out_d)
     qs = batch.query_start
@@ -211,8 +213,9 @@ def run_prefill(cfg, *, rows=None, device_values=False, poison=True, check_pools
         rows = {s: list(range(min(int(ql[s]), mql))) for s in range(cfg.num_seqs)}
     rows = {s: [j for j in js if j < mql] for s, js in rows.items()}
     t1 = time.time()
-    ref = oracle.paged_prefill_ref(P.q, P.kp, P.vp, batch.block_tables, qs, batch.context_lens,
-                                   cfg.scale, seqs=sorted(rows), rows=rows, **P.kw)
+    ctx_ref = np.minimum(batch.context_lens, mcl)
+    ref = oracle.paged_prefill_ref(P.q, P.kp, P.vp, batch.block_tables, qs, ctx_ref, cfg.scale,
+                                   seqs=sorted(rows), rows=rows, **P.kw)
     res["oracle_s"] = time.time() - t1
     err, excess, mx, n = 0.0, -1.0, 0.0, 0
     for (s, j), r in ref.items():

@@ -62,6 +62,16 @@ def test_prefill_max_query_len_truncates():
     log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g}")
 
 
+def test_prefill_max_context_len_truncates():
+    """Contexts longer than max_context_len are truncated to it: the chunk's queries then sit at
+    positions counted from the truncated context."""
+    cfg = small("ctx_trunc_f16", "f16", 3, 4, 2, 128, 16, ("fixed", (400, 250, 330)),
+                ("uniform", 20, 60), 23)
+    log("[prefill] max_context_len=300 over contexts (400, 250, 330)")
+    r = run_prefill(cfg, max_context_len=300)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g}")
+
+
 def test_prefill_empty_sequences_and_zero_len():
     """Sequences without new tokens write nothing; max_query_len 0 launches nothing."""
     cfg = small("empty_f16", "f16", 8, 4, 4, 64, 16, ("uniform", 1, 90), ("uniform", 0, 3), 18)
