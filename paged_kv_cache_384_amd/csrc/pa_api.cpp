@@ -197,6 +197,10 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* va
       !aligned(value, 16) || !aligned(block_tables, 4) || !aligned(token_seq, 4) ||
       !aligned(token_pos, 4))
     return PA_ERR_ALIGN;
+  // one thread per 16-byte piece of every token's heads, 256 per workgroup
+  const int64_t pieces = static_cast<int64_t>(num_tokens) * c->num_kv_heads * c->head_dim *
+                         elem_size(c->dtype) / 16;
+  if ((pieces + 255) / 256 >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
   pa::CacheWriteArgs a;
   a.k_pool = static_cast<uint8_t*>(key_cache);
   a.v_pool = static_cast<uint8_t*>(value_cache);

@@ -10,32 +10,36 @@
 
 namespace pa {
 
-// One workgroup per new token. Each thread moves 16-byte pieces: piece q of KV head h holds
-// elements [q*Epp, q*Epp + Epp) of that head's vector. In the value tile it goes to row `slot`,
-// byte q*16; in the key tile to chunk row q/4 (64-byte chunks = 4 pieces), slot `slot`, byte
-// (q%4)*16 of that slot's 64-byte segment.
+// One thread per 16-byte piece of a new token's key (and the same piece of its value): the
+// pieces of all tokens are numbered token-major, so a workgroup of 256 threads covers whole
+// tokens or parts of one, whatever the head count. Piece q of KV head h holds elements
+// [q*Epp, q*Epp + Epp) of that head's vector. In the value tile it goes to row `slot`, byte
+// q*16; in the key tile to chunk row q/4 (64-byte chunks = 4 pieces), slot `slot`, byte (q%4)*16
+// of that slot's 64-byte segment. The payload is loaded before the slot is looked up, so the
+// table read and the payload load are in flight together.
 template <DType dt, int D, int B>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
   using G = TileGeom<dt, D, B>;
-  const int n = blockIdx.x;
+  constexpr int kPieces = G::kPiecesPerRow;
+  const int per_token = a.num_kv_heads * kPieces;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(a.num_tokens) * per_token) return;
+  const int n = static_cast<int>(i / per_token);
+  const int r = static_cast<int>(i % per_token);
+  const int h = r / kPieces;
+  const int q = r % kPieces;
+  const int64_t src = i * 16;  // token n, head h, piece q of the [T][Hkv][D] inputs
+  const u32x4 kv = load16(a.key + src);
+  const u32x4 vv = load16(a.value + src);
   const int s = a.token_seq[n];
   const int pos = a.token_pos[n];
   if (pos < 0 || pos >= a.max_blocks * B || s < 0 || s >= a.num_seqs) return;
   int blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + pos / B];
   blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
   const int slot = pos % B;
-  constexpr int kPieces = G::kPiecesPerRow;
-  const int total = a.num_kv_heads * kPieces;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int h = i / kPieces;
-    const int q = i % kPieces;
-    const int64_t src = (static_cast<int64_t>(n) * a.num_kv_heads + h) * G::kRowBytes + q * 16;
-    const int64_t tile = (static_cast<int64_t>(blk) * a.num_kv_heads + h) * G::kTileBytes;
-    const u32x4 kv = load16(a.key + src);
-    const u32x4 vv = load16(a.value + src);
-    store16(a.k_pool + tile + (q >> 2) * G::kChunkRowBytes + slot * 64 + (q & 3) * 16, kv);
-    store16(a.v_pool + tile + slot * G::kRowBytes + q * 16, vv);
-  }
+  const int64_t tile = (static_cast<int64_t>(blk) * a.num_kv_heads + h) * G::kTileBytes;
+  store16(a.k_pool + tile + (q >> 2) * G::kChunkRowBytes + slot * 64 + (q & 3) * 16, kv);
+  store16(a.v_pool + tile + slot * G::kRowBytes + q * 16, vv);
 }
 
 // Grid: num_pairs * chunks workgroups; each copies its chunk of one block in both pools. A
@@ -62,8 +66,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a, int chunks
 
 template <DType dt, int D, int B>
 static hipError_t launch_rc(const CacheWriteArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((reshape_and_cache_kernel<dt, D, B>), dim3(a.num_tokens), dim3(256), 0,
-                     stream, a);
+  const int64_t pieces =
+      static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * TileGeom<dt, D, B>::kPiecesPerRow;
+  hipLaunchKernelGGL((reshape_and_cache_kernel<dt, D, B>),
+                     dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
