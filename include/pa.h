@@ -62,7 +62,7 @@ extern "C" {
 #define PA_API
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -297,6 +297,38 @@ PA_API pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* v
 PA_API pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_value,
                          const pa_cache_desc* src, const void* src_key, const void* src_value,
                          const int32_t* src_dst, int32_t num_pairs, void* stream);
+
+/*
+ * pa_validate_tables — count violations of the device-side caller contract of pa_decode,
+ * pa_decode_contiguous, pa_prefill and pa_reshape_and_cache, without reading the pools.
+ * ([anal] §2 and the lookup pseudocode: a logical block is resolved through the sequence's block
+ *  table to a physical block of the pool; the kernels clamp a block id outside the pool instead of
+ *  faulting, so a corrupt table would otherwise go unnoticed.)
+ *
+ * For each sequence s with n = context_lens[s], one violation is counted for each of:
+ *   n < 0 or n > max_context_len (the attention calls would truncate it);
+ *   each table entry block_tables[s][j], j < ceil(min(max(n, 0), max_context_len) / B) (the
+ *     entries the attention calls read), outside [0, c->num_blocks);
+ *   with query_start given: query_start[0] != 0 (counted once, for s = 0),
+ *     query_start[s+1] < query_start[s], or q_len = query_start[s+1] - query_start[s] > n.
+ * The count is written to *violations (device int32, 4-byte aligned); the library clears it
+ * first with a kernel of its own, so the call can be captured in a graph. Entries past a
+ * sequence's used range are not read. num_seqs * (max_blocks_per_seq + 3) must stay below 2^31
+ * so that the count cannot overflow.
+ *
+ *   block_tables            device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens            device int32 [num_seqs]
+ *   query_start             device int32 [num_seqs + 1], or NULL (decode: no query ranges)
+ *   max_context_len         as passed to the attention call, <= max_blocks_per_seq * B
+ *   violations              device int32 [1], written
+ * Only c->block_size and c->num_blocks matter (the rest of *c is checked as everywhere).
+ * Errors: checked on the host before any launch (PA_ERR_NULL / SHAPE / UNSUPPORTED / ALIGN); a
+ * failed launch gives PA_ERR_LAUNCH. num_seqs = 0 writes 0.
+ */
+PA_API pa_status pa_validate_tables(const pa_cache_desc* c, const int32_t* block_tables,
+                                    int32_t num_seqs, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, const int32_t* query_start,
+                                    int32_t max_context_len, int32_t* violations, void* stream);
 
 /* Static description of a status code (never NULL). */
 PA_API const char* pa_status_string(pa_status s);

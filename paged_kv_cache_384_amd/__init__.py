@@ -23,11 +23,12 @@ import os
 
 __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
-    "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_status_string",
+    "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks",
+    "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_validate_tables", "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,8 +36,8 @@ library_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
-                    "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string",
-                    "pa_abi_version"]
+                    "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_validate_tables",
+                    "pa_status_string", "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.pa_swap_blocks.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_desc_p, _vp, _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_validate_tables.argtypes = [_desc_p, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
+        L.pa_validate_tables.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
@@ -314,6 +317,32 @@ def pa_copy_blocks(key_cache, value_cache, src_dst, *, head_dim: int, block_size
             _dev(src_dst, "src_dst", torch.int32), pairs.shape[0] if src_dst.numel() else 0,
             _stream(key_cache, stream))
     _check(lib().pa_copy_blocks(*args), "pa_copy_blocks")
+
+
+def pa_validate_tables(key_cache, block_tables, context_lens, max_context_len: int,
+                       violations=None, *, head_dim: int, query_start=None,
+                       block_size: int | None = None, stream=None):
+    """Count violations of the device-side contract (context lengths, the table entries the
+    attention calls read, and query ranges if ``query_start`` is given) into ``violations``
+    (a GPU int32 tensor of one element, allocated if None), which is returned."""
+    import torch
+    d = _desc(key_cache, head_dim, block_size)
+    if block_tables.dim() != 2 or context_lens.shape != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    num_seqs = block_tables.shape[0]
+    if query_start is not None and query_start.shape != (num_seqs + 1,):
+        raise ValueError("query_start must be [num_seqs + 1]")
+    if violations is None:
+        violations = torch.empty(1, dtype=torch.int32, device=key_cache.device)
+    if violations.numel() != 1:
+        raise ValueError("violations must hold one int32")
+    args = (ctypes.byref(d), _dev(block_tables, "block_tables", torch.int32), num_seqs,
+            block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+            _vp(0) if query_start is None else _dev(query_start, "query_start", torch.int32),
+            int(max_context_len), _dev(violations, "violations", torch.int32),
+            _stream(key_cache, stream))
+    _check(lib().pa_validate_tables(*args), "pa_validate_tables")
+    return violations
 
 
 def pa_swap_blocks(dst_key, dst_value, src_key, src_value, src_dst, *, head_dim: int,

@@ -352,6 +352,39 @@ pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_ca
   return PA_OK;
 }
 
+pa_status pa_validate_tables(const pa_cache_desc* c, const int32_t* block_tables,
+                             int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start,
+                             int32_t max_context_len, int32_t* violations, void* stream) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_context_len) >
+      static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+    return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(num_seqs) * (static_cast<int64_t>(max_blocks_per_seq) + 3) >=
+      (int64_t{1} << 31))
+    return PA_ERR_SHAPE;
+  if (!violations) return PA_ERR_NULL;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PA_ERR_NULL;
+  if (!aligned(violations, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  pa::ValidateArgs a;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.violations = violations;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = c->num_blocks;
+  a.block_size = c->block_size;
+  a.max_ctx = max_context_len;
+  if (pa::launch_validate(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_value,
                          const pa_cache_desc* src, const void* src_key, const void* src_value,
                          const int32_t* src_dst, int32_t num_pairs, void* stream) {

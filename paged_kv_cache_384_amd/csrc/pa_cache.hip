@@ -107,4 +107,45 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// pa_validate_tables. The count is cleared by its own one-thread kernel (no memset node in a
+// captured graph), then each workgroup checks one sequence: thread 0 its length and query range,
+// all threads the table entries the attention calls would read; each wavefront adds its count
+// with one atomic.
+__global__ void clear_count_kernel(int32_t* count) {
+  if (threadIdx.x == 0) count[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
+  const int s = static_cast<int>(blockIdx.x);
+  const int n = a.context_lens[s];
+  int bad = 0;
+  if (threadIdx.x == 0) {
+    bad += (n < 0 || n > a.max_ctx) ? 1 : 0;
+    if (a.query_start != nullptr) {
+      const int q0 = a.query_start[s];
+      const int q1 = a.query_start[s + 1];
+      bad += (s == 0 && q0 != 0) ? 1 : 0;
+      bad += (q1 < q0 || q1 - q0 > (n < 0 ? 0 : n)) ? 1 : 0;
+    }
+  }
+  const int used = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int nb = (used + a.block_size - 1) / a.block_size;
+  const int32_t* row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  for (int j = static_cast<int>(threadIdx.x); j < nb; j += 256) {
+    const int id = row[j];
+    bad += (id < 0 || id >= a.num_blocks) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+  if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(a.violations, bad);
+}
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(64), 0, stream, a.violations);
+  if (a.num_seqs > 0)
+    hipLaunchKernelGGL(validate_kernel, dim3(static_cast<unsigned>(a.num_seqs)), dim3(256), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace pa

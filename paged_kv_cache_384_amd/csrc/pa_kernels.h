@@ -42,6 +42,19 @@ struct CopyArgs {
   int64_t block_bytes;  // bytes of one physical block in one pool (all KV heads)
 };
 
+// Table and length checks of pa_validate_tables: one workgroup per sequence.
+struct ValidateArgs {
+  const int32_t* block_tables;  // [num_seqs][max_blocks]
+  const int32_t* context_lens;  // [num_seqs]
+  const int32_t* query_start;   // [num_seqs + 1] or null
+  int32_t* violations;          // [1]
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_ctx;
+};
+
 // One launch of the attention stage covers every (KV head, sequence, head group, partition).
 struct DecodeArgs {
   const uint8_t* k_pool;
@@ -106,6 +119,7 @@ constexpr int kPrefillSeqMajorTiles = 4;
 hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
                                     const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 hipError_t launch_decode_attention_b8(DType dt, int head_dim, const DecodeArgs& a,
                                       hipStream_t stream);
 hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs& a,

@@ -265,6 +265,29 @@ def test_prefill_validation(L):
     assert pf(desc(dtype=2, d=64, b=8), S=0, max_ctx=65, ptrs=none) == SHAPE
 
 
+def test_validate_tables_validation(L):
+    """Sizes, pointers and alignment checked before the launch; query_start may be NULL."""
+    def vt(d=None, *, S=2, maxb=8, max_ctx=100, ptrs=None):
+        d = desc() if d is None else d
+        p = ptrs or {}
+        return L.pa_validate_tables(ctypes.byref(d) if d is not False else None,
+                                    p.get("bt", GOOD), S, maxb, p.get("ctx", GOOD),
+                                    p.get("qs", GOOD), max_ctx, p.get("out", GOOD), P(0))
+    assert vt(False) == NULL
+    assert vt(desc(d=96)) == UNSUP
+    assert vt(desc(b=64)) == UNSUP
+    assert vt(S=-1) == SHAPE
+    assert vt(maxb=0) == SHAPE
+    assert vt(max_ctx=-1) == SHAPE
+    assert vt(max_ctx=8 * 16 + 1) == SHAPE               # longer than the table
+    assert vt(S=1 << 24, maxb=1 << 8, max_ctx=16) == SHAPE  # count could overflow int32
+    for k in ("bt", "ctx", "out"):
+        assert vt(ptrs={k: P(0)}) == NULL, k
+    assert vt(S=0, ptrs={"bt": P(0), "ctx": P(0), "qs": P(0), "out": P(0)}) == NULL
+    for k in ("bt", "ctx", "qs", "out"):
+        assert vt(ptrs={k: P(0x10002)}) == ALIGN, k
+
+
 def test_binding_rejects_host_tensors_and_bad_shapes():
     """The Python binding checks placement and shapes before any call reaches the library."""
     import torch
