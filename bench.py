@@ -542,7 +542,9 @@ def main():
                    "context_lens": list(cfg.ctx), "num_blocks": batch.num_blocks,
                    "partition_size": part, "max_context_len": batch.max_context_len,
                    "kv_bytes_per_step": kv_bytes, "accumulate": "f32",
-                   "copy_pairs": int(n_pairs), "shared_blocks": bool(shared)},
+                   "copy_pairs": int(n_pairs), "shared_blocks": bool(shared),
+                   "blocks_distinct": batch.block_counts()[0],
+                   "blocks_if_unshared": batch.block_counts()[1]},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
         "tokens_per_s_attention_only": round(

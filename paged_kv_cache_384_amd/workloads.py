@@ -347,6 +347,15 @@ class DecodeBatch:
         """Whether some physical block is referenced by more than one sequence's table."""
         return bool((self.ref_counts > 1).any())
 
+    def block_counts(self) -> tuple:
+        """(distinct physical blocks the tables reference, blocks the same contexts would take
+        if no block were shared): the block-count saving of prefix sharing for this batch."""
+        B = self.cfg.block_size
+        nb = (self.context_lens.astype(np.int64) + B - 1) // B
+        used = [self.block_tables[s, :nb[s]] for s in range(self.cfg.num_seqs)]
+        distinct = int(np.unique(np.concatenate(used)).size) if used else 0
+        return distinct, int(nb.sum())
+
     def kv_bytes(self) -> int:
         """K plus V bytes the attention must read: every context token, every KV head."""
         c = self.cfg

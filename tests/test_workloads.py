@@ -132,6 +132,26 @@ def test_unshared_configs_own_their_blocks():
     for name in ("tiny_fp32", "opt13b_fp16", "gqa_bf16", "long_bf16"):
         b = wl.build_batch(wl.CONFIGS[name])
         assert b.ref_counts.max() == 1 and b.copy_pairs.shape[0] == 0
+        distinct, unshared = b.block_counts()
+        assert distinct == unshared
+
+
+def test_shared_prefix_block_saving():
+    """The shared-prefix batch: 32 prompts of 520 tokens, 8 samples each. Shared: per prompt 32
+    full prompt blocks once, 8 partial prompt blocks (the original and 7 copies) and each
+    sample's suffix blocks; unshared: every sample's whole context."""
+    cfg = wl.CONFIGS["cow_fp16"]
+    b = wl.build_batch(cfg)
+    B = cfg.block_size
+    prompt, n = cfg.ctx[1], cfg.ctx[4]
+    distinct, unshared = b.block_counts()
+    nb = (b.context_lens + B - 1) // B
+    assert unshared == int(nb.sum())
+    prompts = cfg.num_seqs // n
+    full = prompt // B
+    # each sample owns every block from the partial prompt block on
+    assert distinct == prompts * full + int((nb - full).sum())
+    assert distinct < unshared
 
 
 def test_shared_prefix_structure():
