@@ -74,6 +74,18 @@ def test_table_capacity_and_largest_partition():
         run_step(cfg, partition_size=part)
 
 
+def test_very_long_contexts():
+    """Contexts of 131 072 and 70 001 tokens (4096-entry table rows at B = 32): 128 and 256
+    partitions per head at the library's and at 512-token partitions, merged by the multi-group
+    reduce kernel."""
+    cfg = wl.DecodeConfig("very_long_bf16", "bf16", num_seqs=2, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, block_size=32, ctx=("fixed", (131072, 70001)), seed=37)
+    for part in (0, 512):
+        log(f"[parity] very long contexts partition={part}")
+        r = run_step(cfg, partition_size=part)
+        log(f"    max_abs_err={r['max_abs_err']:.3g} oracle {r['oracle_s']:.1f}s")
+
+
 def test_all_empty():
     cfg = wl.DecodeConfig("empty", "f16", num_seqs=3, num_q_heads=4, num_kv_heads=2,
                           head_dim=64, ctx=("fixed", (0, 0, 0)), seed=31)
