@@ -104,6 +104,21 @@ def test_prefill_long_context_chunks():
         f"{r['excess_err']:.3g}")
 
 
+def test_prefill_long_prompts():
+    """Whole prompts of 8192 and 5000 tokens (64 and 40 query tiles per sequence, tile-major
+    units), bf16 GQA at B = 16: sampled queries on both sides of tile edges, first and last."""
+    cfg = small("long_prompt_bf16", "bf16", 2, 8, 2, 128, 16, ("fixed", (8192, 5000)), ("all",), 24)
+    P = Prepared(cfg, device_values=True)
+    ql = P.batch.query_lens
+    rng = np.random.default_rng(9)
+    rows = {s: sorted({0, 1, 63, 64, 127, 128, int(ql[s]) // 2, int(ql[s]) - 1} |
+                      set(rng.integers(0, ql[s], 8).tolist())) for s in range(cfg.num_seqs)}
+    log(f"[prefill] long prompts q={ql.tolist()}")
+    r = run_prefill(cfg, rows=rows, prepared=P)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} beyond output rounding "
+        f"{r['excess_err']:.3g}")
+
+
 @pytest.mark.parametrize("name", ["prefill_bf16", "chunked_fp16"])
 @pytest.mark.timeout(900)
 def test_prefill_full_size(name):
