@@ -16,8 +16,9 @@
 // sequence's tokens in tiles of 64, from token 0 to the last position its queries can see:
 //   * the tile's key rows and value rows are gathered through the block table into LDS (double
 //     buffered, the next tile's global loads in flight while the current one is computed), one
-//     288-byte row per token for each (72 dwords, 8 more than a multiple of the 64 banks: the
-//     operand reads below are free of bank conflicts at that stride on gfx950, measured);
+//     row per token for each, the head vector plus 32 bytes: 288 bytes at head_dim 128 (72
+//     dwords, 8 more than a multiple of the 64 banks: the operand reads below are free of bank
+//     conflicts at that stride on gfx950, measured), 160 bytes at head_dim 64 (40 dwords);
 //   * each wavefront forms S^T = K Q^T: A = 16 tokens x 32 dims read from LDS, B = its queries
 //     held in registers since the start. Lane l gets query l%16 and tokens 4(l/16)..4(l/16)+3 of
 //     each 16-token block;
@@ -92,16 +93,20 @@ template <> struct Pack2<DType::BF16> {
 
 }  // namespace
 
-// Two workgroups per CU (eight wavefronts, two per SIMD): registers are capped at 256 per lane
-// so one wavefront's softmax overlaps the other's matrix-core work.
+// Workgroups per CU: two at head_dim 128 (eight wavefronts, two per SIMD, registers capped at
+// 256 per lane, 72 KiB of LDS each), three at head_dim 64 (registers capped at 168, 40 KiB of
+// LDS each), so one wavefront's softmax overlaps another's matrix-core work.
+template <int D> constexpr int prefill_waves_per_simd() { return D == 64 ? 3 : 2; }
+
 template <DType dt, int D, int B>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(
+    prefill_waves_per_simd<D>(), prefill_waves_per_simd<D>())))
 void prefill_kernel(PrefillArgs a) {
   using G = TileGeom<dt, D, B>;
   static_assert(G::kEsz == 2, "matrix-core prefill takes 16-bit elements");
   constexpr int kChunks = D / 32;          // 64-byte chunks (32 dims) per key row
   constexpr int kDBlocks = D / 16;         // 16-dim output blocks
-  constexpr int kRow = 288;                // LDS row of one token (keys or values), padded
+  constexpr int kRow = D * 2 + 32;         // LDS row of one token (keys or values), padded
   constexpr int kVPieces = D / 32;         // 16-byte value pieces per lane per tile
   static_assert(D * 2 <= kRow, "a token's head vector fits one LDS row");
   __shared__ __align__(16) uint8_t k_s[2][kTileT * kRow];
