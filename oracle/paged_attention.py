@@ -209,11 +209,13 @@ def paged_prefill_ref(query, k_pool, v_pool, block_tables, query_start, context_
         js = range(q_len) if rows is None else rows[s]
         for j in js:
             p = ctx - q_len + j
+            # a query at a negative position (q_len > ctx) sees no token: a zero row, as for
+            # an empty context
+            n = max(p + 1, 0)
             o = np.zeros((Hq, d))
             for h in range(Hq):
                 g = h // G
-                o[h] = attention_one_query(q64[q0 + j, h], K[:p + 1, g, :], V[:p + 1, g, :],
-                                           scale64)
+                o[h] = attention_one_query(q64[q0 + j, h], K[:n, g, :], V[:n, g, :], scale64)
             out[(s, j)] = o
     return out
 

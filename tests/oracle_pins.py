@@ -512,6 +512,24 @@ def pin_prefill_decode_and_chunks(oracle):
         assert np.array_equal(full[(0, 0)][h], v0[h // 2])
 
 
+def pin_prefill_longer_than_context(oracle):
+    """A chunk longer than its context (q_len > ctx, outside the callers' contract): its first
+    q_len - ctx queries sit at negative positions and see no token, giving zero rows; the others
+    are the rows of the same queries with q_len = ctx."""
+    rng = np.random.default_rng(79)
+    n, extra = 10, 6
+    c = _prefill_case(rng, dtype="f16", S=1, Hq=4, Hkv=2, d=64, ctx=(n,), q_lens=(n + extra,))
+    out = _prefill(oracle, c)
+    for j in range(extra):
+        assert np.array_equal(out[(0, j)], np.zeros((4, 64))), j
+    fit = dict(c)
+    fit["Q"] = c["Q"][extra:]
+    fit["qs"] = np.array([0, n], np.int32)
+    ref = _prefill(oracle, fit)
+    for j in range(n):
+        assert np.array_equal(out[(0, extra + j)], ref[(0, j)])
+
+
 def pin_swap_blocks(oracle):
     """Swapping blocks into another pool changes exactly the destination blocks, each becoming
     a bit copy of its source block in both pools; swapping out and back in restores the blocks;
@@ -541,4 +559,4 @@ ALL_PINS = [pin_widening, pin_layout, pin_slot_enumeration, pin_cache_round_trip
             pin_cache_write_footprint, pin_copy_blocks, pin_sdpa, pin_closed_forms,
             pin_paging_invariance, pin_block_size_invariance, pin_sharing_invariance,
             pin_poison_ignored, pin_blockwise_online, pin_split_merge, pin_prefill_sdpa,
-            pin_prefill_decode_and_chunks, pin_swap_blocks]
+            pin_prefill_decode_and_chunks, pin_prefill_longer_than_context, pin_swap_blocks]
