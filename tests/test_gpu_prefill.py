@@ -17,7 +17,9 @@ import torch
 
 import paged_kv_cache_384_amd as pa
 from paged_kv_cache_384_amd import workloads as wl
-from _gpu_cases import Prepared, log, run_prefill
+import oracle
+from _gpu_cases import Prepared, excess_error, log, run_prefill
+from _helpers import to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +72,36 @@ def test_prefill_max_context_len_truncates():
     log("[prefill] max_context_len=300 over contexts (400, 250, 330)")
     r = run_prefill(cfg, max_context_len=300)
     log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g}")
+
+
+def test_prefill_chunk_longer_than_context():
+    """A chunk longer than its context (q_len > n, outside the callers' contract but defined in
+    include/pa.h): its first q_len - n queries get zero rows, the rest attend as usual."""
+    cfg = small("over_f16", "f16", 3, 4, 2, 128, 16, ("fixed", (150, 90, 300)),
+                ("uniform", 40, 80), 25)
+    P = Prepared(cfg)
+    P.write_cache(check_pools=False)
+    b = P.batch
+    ctx2 = b.context_lens.copy()
+    ctx2[0] = int(b.query_lens[0]) - 7      # 7 queries before position 0
+    ctx2[2] = 3                             # all but 3 queries before position 0
+    log(f"[prefill] q_len > ctx: q={b.query_lens.tolist()} ctx={ctx2.tolist()}")
+    out_d = torch.full_like(P.q_d, float("nan"))
+    pa.pa_prefill(out_d, P.q_d, P.kp_d, P.vp_d, P.bt_d, P.qs_d,
+                  torch.from_numpy(ctx2).to(P.q_d.device), cfg.scale, b.max_query_len,
+                  b.max_context_len)
+    torch.cuda.synchronize()
+    out = to_storage(out_d)
+    ref = oracle.paged_prefill_ref(P.q, P.kp, P.vp, b.block_tables, b.query_start, ctx2,
+                                   cfg.scale, **P.kw)
+    worst = 0.0
+    for (s, j), r in ref.items():
+        got = oracle.to_f64(out[int(b.query_start[s]) + j], cfg.dtype)
+        if int(ctx2[s]) - int(b.query_lens[s]) + j < 0:
+            assert np.array_equal(got, np.zeros_like(got)), (s, j)
+        worst = max(worst, excess_error(got, r, cfg.dtype))
+    log(f"    {len(ref)} rows, error beyond output rounding {worst:.3g}")
+    assert worst <= 1e-2
 
 
 def test_prefill_empty_sequences_and_zero_len():
