@@ -423,7 +423,9 @@ const char* pa_status_string(pa_status s) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
-    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or block_size";
+    case PA_ERR_UNSUPPORTED:
+      return "unsupported configuration (dtype, head_dim, block_size, flags) or memory the device "
+             "cannot address";
     case PA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for data, 4 for int32 arrays)";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_decode_workspace_bytes()";
     case PA_ERR_LAUNCH: return "the HIP runtime reported a launch error";

@@ -76,3 +76,31 @@ def test_swap_round_trip(dt, b):
                                   cfg.scale, **kw)
     tol = 1e-5 if dt == "f32" else 1e-2
     assert float(np.abs(oracle.to_f64(to_storage(out1), dt) - ref).max()) <= tol
+
+
+def test_swap_refuses_pageable_host_memory():
+    """The C entry point itself (the binding refuses such tensors before calling it) answers
+    PA_ERR_UNSUPPORTED for a pool in ordinary pageable host memory, launches nothing and leaves
+    no HIP error behind: the next call works."""
+    import ctypes
+    dev = torch.device("cuda:0")
+    L = pa.lib()
+    d = pa.CacheDesc(pa.DTYPE_CODES["f16"], 8, 2, 64, 16, 0)
+    gk = torch.zeros((8, 2, 16 * 64), dtype=torch.float16, device=dev)
+    gv = torch.zeros_like(gk)
+    hk = np.zeros((8, 2, 16 * 64), np.float16)   # pageable
+    hv = np.zeros_like(hk)
+    pairs = torch.tensor([[1, 2]], dtype=torch.int32, device=dev)
+    vp = ctypes.c_void_p
+    st = L.pa_swap_blocks(ctypes.byref(d), vp(hk.ctypes.data), vp(hv.ctypes.data), ctypes.byref(d),
+                          vp(gk.data_ptr()), vp(gv.data_ptr()), vp(pairs.data_ptr()), 1, vp(0))
+    log(f"[swap] pageable destination: status {st} ({pa.pa_status_string(st)})")
+    assert st == 3  # PA_ERR_UNSUPPORTED
+    st = L.pa_swap_blocks(ctypes.byref(d), vp(gk.data_ptr()), vp(gv.data_ptr()), ctypes.byref(d),
+                          vp(hk.ctypes.data), vp(hv.ctypes.data), vp(pairs.data_ptr()), 1, vp(0))
+    assert st == 3
+    assert np.all(hk == 0) and np.all(hv == 0)
+    gk[1] = 1.0
+    pa.pa_copy_blocks(gk, gv, pairs.reshape(-1), head_dim=64)
+    torch.cuda.synchronize()
+    assert torch.equal(gk[2], gk[1]) and bool((gk[2] == 1.0).all())
