@@ -71,7 +71,8 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
-  PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim, block_size or flag the kernels do not support */
+  PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim, block_size or flag the kernels do not support, or
+                             memory the device cannot address (pa_swap_blocks) */
   PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned (int arrays: 4-byte) */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_decode_workspace_bytes() */
   PA_ERR_LAUNCH = 6,      /* the HIP runtime reported an error when launching */
