@@ -5,7 +5,8 @@ this package. It imports nothing from the HIP library and the library imports no
 """
 from .paged_attention import (  # noqa: F401
     attention_one_query,
-    blockwise_online_ref,
+    blocked_form_ref,
+    causal_rows,
     copy_blocks_ref,
     gather_sequence_kv,
     k_offset,

@@ -16,9 +16,9 @@ Sources, cited by page title and section (the same four pages throughout):
           o_i summed over the first ceil(i/B) blocks).
   [anal]  "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net), §2 (KV blocks of
           B tokens in scattered physical memory, on-demand allocation), §3 (the block-wise
-          kernel gives the same result as ordinary attention, only partial sums are blocked),
-          the block-table lookup pseudocode (running max starting at -inf, running denominator,
-          running output, final division), §4 (copy-on-write of a shared block).
+          kernel gives the same result as ordinary attention, only partial sums are blocked;
+          a logical block is found through the sequence's block table), §4 (copy-on-write of a
+          shared block).
   [blog]  "PagedAttention 논문 쉽게 읽기" (iplexlaw.co.kr), §2: a token is written into the free
           slot of its sequence's last block; ②: copy-on-write of a shared last block.
   [dev]   "추론 엔진에서의 메모리 가상화: PagedAttention과 메모리 단편화의 제거" (molayo1419.me):
@@ -179,8 +179,37 @@ def paged_decode_ref(query, k_pool, v_pool, block_tables, context_lens, scale, *
     return out
 
 
+def causal_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, last: np.ndarray, scale: float,
+                moments: bool = False):
+    """The dense causal form for several query rows at once ([wiki] dense form for a general
+    query token i: it attends to tokens 1..i and to nothing after).
+
+    Q [r, d]; K, V [n, d]; row r attends to tokens 0..last[r] (last[r] < 0: no token, a zero
+    row). Returns O [r, d], and with ``moments`` also M2 [r, d] = sum_t w_t v_t^2, the second
+    moment of the values under the row's softmax weights w (what a rounding bound on a weighted
+    mean needs: sum_t w_t |v_t - o| <= sqrt(M2 - o^2)).
+    """
+    r, d = Q.shape
+    O = np.zeros((r, d))
+    M2 = np.zeros((r, d))
+    if r and K.shape[0]:
+        Z = scale * (Q @ K.T)
+        visible = np.arange(K.shape[0])[None, :] <= np.asarray(last)[:, None]
+        Z = np.where(visible, Z, -np.inf)
+        seen = visible.any(axis=1)
+        top = np.where(seen, Z.max(axis=1, initial=-np.inf), 0.0)
+        W = np.exp(Z - top[:, None])                # exp(-inf) = 0 outside the causal range
+        den = W.sum(axis=1)
+        den = np.where(seen, den, 1.0)
+        O = (W @ V) / den[:, None]
+        if moments:
+            M2 = (W @ (V * V)) / den[:, None]
+    return (O, M2) if moments else O
+
+
 def paged_prefill_ref(query, k_pool, v_pool, block_tables, query_start, context_lens, scale, *,
-                      dtype, num_kv_heads, block_size, head_dim, seqs=None, rows=None):
+                      dtype, num_kv_heads, block_size, head_dim, seqs=None, rows=None,
+                      moments=False):
     """Causal attention of every query token over its sequence's paged KV cache ([wiki] dense
     form for a general query i: token i attends to tokens 1..i; the blocked form sums over the
     first ceil(i/B) blocks).
@@ -188,9 +217,10 @@ def paged_prefill_ref(query, k_pool, v_pool, block_tables, query_start, context_
     Sequence s's queries are rows query_start[s] .. query_start[s+1]-1 of ``query`` (stored
     [T, Hq, d]); they are its newest q_len = query_start[s+1] - query_start[s] tokens, so query j
     sits at position p = ctx - q_len + j (0-based) and attends to tokens 0..p of the cache
-    (q_len = 1 is a decode step, q_len = ctx a whole prompt). ``seqs`` selects sequences,
-    ``rows`` (a dict seq -> list of j) selects queries within them. Returns a dict
-    (s, j) -> float64 [Hq, d].
+    (q_len = 1 is a decode step, q_len = ctx a whole prompt; a negative p, q_len > ctx, sees no
+    token and gives a zero row, as an empty context does). ``seqs`` selects sequences, ``rows``
+    (a dict seq -> list of j) selects queries within them. Returns a dict (s, j) -> float64
+    [Hq, d]; with ``moments`` a dict (s, j) -> (o, M2), M2 as in ``causal_rows``.
     """
     q64 = to_f64(query, dtype)
     T, Hq, d = q64.shape
@@ -206,57 +236,55 @@ def paged_prefill_ref(query, k_pool, v_pool, block_tables, query_start, context_
         K, V = gather_sequence_kv(k_pool, v_pool, block_tables[s], ctx, dtype=dtype,
                                   num_kv_heads=num_kv_heads, block_size=block_size,
                                   head_dim=head_dim)
-        js = range(q_len) if rows is None else rows[s]
-        for j in js:
-            p = ctx - q_len + j
-            # a query at a negative position (q_len > ctx) sees no token: a zero row, as for
-            # an empty context
-            n = max(p + 1, 0)
-            o = np.zeros((Hq, d))
-            for h in range(Hq):
-                g = h // G
-                o[h] = attention_one_query(q64[q0 + j, h], K[:n, g, :], V[:n, g, :], scale64)
-            out[(s, j)] = o
+        js = np.asarray(range(q_len) if rows is None else rows[s], dtype=np.int64)
+        if js.size == 0:
+            continue
+        last = ctx - q_len + js                     # position of query j
+        o = np.zeros((js.size, Hq, d))
+        m2 = np.zeros((js.size, Hq, d))
+        for h in range(Hq):
+            g = h // G
+            res = causal_rows(q64[q0 + js, h], K[:, g, :], V[:, g, :], last, scale64, moments)
+            if moments:
+                o[:, h], m2[:, h] = res
+            else:
+                o[:, h] = res
+        for n, j in enumerate(js.tolist()):
+            out[(s, j)] = (o[n], m2[n]) if moments else o[n]
     return out
 
 
 # ---------------------------------------------------------------------------------------------
-# The pages' block-by-block loop (a second form, used to check the first)
+# The blocked form (a second form, used to check the first)
 # ---------------------------------------------------------------------------------------------
 
-def blockwise_online_ref(q, k_pool, v_pool, block_table_row, ctx, scale, g, *, dtype,
-                         num_kv_heads, block_size, head_dim):
-    """One query head over one sequence, block by block with a running softmax.
+def blocked_form_ref(q, k_pool, v_pool, block_table_row, ctx, scale, g, *, dtype,
+                     num_kv_heads, block_size, head_dim):
+    """One query head over one sequence in [wiki]'s blocked form: with K_j, V_j the keys and
+    values of logical block j (the physical block the table names), the weight vector of block
+    j is exp(scale * K_j q) divided by the sum of every entry of every block's vector, and the
+    output is the sum over blocks of V_j^T times that vector.
 
-    Follows the block-table lookup pseudocode of [anal]: output, denominator and running
-    maximum start at 0, 0 and -inf; for each logical block, look up its physical block, take its
-    keys and values, score them, fold them into the running state; divide at the end. The
-    running-state update, which the pseudocode names but does not spell out, is the usual one:
-    new max m' = max(m, block scores); old state rescaled by exp(m - m'); new terms weighted
-    by exp(score - m'). Slots at or past ``ctx`` in the last block are left out.
-    q: float64 [d]. Returns float64 [d].
+    Every block's exponentials are taken relative to one common constant (the largest score of
+    the sequence), which cancels in the ratio and keeps them finite. Slots at or past ``ctx`` in
+    the last block are not part of K_j, V_j. q: float64 [d]. Returns float64 [d].
     """
     scale64 = float(np.float32(scale))
-    out = np.zeros(head_dim)
-    denom = 0.0
-    running_max = -np.inf
     num_blocks = -(-int(ctx) // block_size)
-    for j in range(num_blocks):
-        phys = int(block_table_row[j])
-        valid = min(block_size, int(ctx) - j * block_size)
-        slots = np.arange(valid)
-        K, V = token_kv(k_pool, v_pool, np.full(valid, phys), slots, dtype=dtype,
-                        num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
-        s = scale64 * (K[:, g, :] @ q)
-        new_max = max(running_max, float(s.max()))
-        rescale = np.exp(running_max - new_max)     # exp(-inf) = 0 on the first block
-        p = np.exp(s - new_max)
-        denom = denom * rescale + p.sum()
-        out = out * rescale + p @ V[:, g, :]
-        running_max = new_max
     if num_blocks == 0:
-        return out
-    return out / denom
+        return np.zeros(head_dim)
+    scores, values = [], []
+    for j in range(num_blocks):
+        valid = min(block_size, int(ctx) - j * block_size)
+        K, V = token_kv(k_pool, v_pool, np.full(valid, int(block_table_row[j])),
+                        np.arange(valid), dtype=dtype, num_kv_heads=num_kv_heads,
+                        block_size=block_size, head_dim=head_dim)
+        scores.append(scale64 * (K[:, g, :] @ q))
+        values.append(V[:, g, :])
+    shift = max(float(z.max()) for z in scores)
+    vectors = [np.exp(z - shift) for z in scores]
+    denominator = sum(float(e.sum()) for e in vectors)
+    return sum(V.T @ e for V, e in zip(values, vectors)) / denominator
 
 
 # ---------------------------------------------------------------------------------------------

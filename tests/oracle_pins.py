@@ -410,17 +410,20 @@ def pin_poison_ignored(oracle):
 # the second form (block loop) and the split merge against the first
 # ---------------------------------------------------------------------------------------------
 
-def pin_blockwise_online(oracle):
+def pin_blocked_form(oracle):
+    """[wiki]'s blocked form (per-block weight vectors over one common denominator, block
+    outputs summed) equals the dense form: only the grouping of the sums differs ([anal] §3)."""
     rng = np.random.default_rng(61)
-    c = make_case(rng, dtype="bf16", S=4, Hq=4, Hkv=2, d=128, ctx=(1, 16, 17, 300))
-    ref = decode(oracle, c)
-    q64 = _widen_torch(c["q"], "bf16").numpy()
-    for s in range(c["S"]):
-        for h in range(c["Hq"]):
-            o = oracle.blockwise_online_ref(q64[s, h], c["k_pool"], c["v_pool"], c["tables"][s],
+    for B, ctx in ((16, (1, 16, 17, 300)), (8, (9, 40, 2, 64))):
+        c = make_case(rng, dtype="bf16", S=4, Hq=4, Hkv=2, d=128, B=B, ctx=ctx)
+        ref = decode(oracle, c)
+        q64 = _widen_torch(c["q"], "bf16").numpy()
+        for s in range(c["S"]):
+            for h in range(c["Hq"]):
+                o = oracle.blocked_form_ref(q64[s, h], c["k_pool"], c["v_pool"], c["tables"][s],
                                             c["ctx"][s], c["scale"], h // 2, dtype="bf16",
-                                            num_kv_heads=2, block_size=16, head_dim=128)
-            assert np.abs(o - ref[s, h]).max() <= 1e-13
+                                            num_kv_heads=2, block_size=B, head_dim=128)
+                assert np.abs(o - ref[s, h]).max() <= 1e-13
 
 
 def pin_split_merge(oracle):
@@ -555,8 +558,36 @@ def pin_swap_blocks(oracle):
     assert all(np.array_equal(a, b) for a, b in zip(within, cow))
 
 
+def pin_causal_moments(oracle):
+    """The second moment the prefill rounding bound uses, against brute force: each weight
+    computed on its own with math.exp, then sum w v^2; and the bound it gives on the mean
+    absolute deviation (sum w |v - o| <= sqrt(M2 - o^2)) holds."""
+    rng = np.random.default_rng(83)
+    n, d, r = 7, 5, 9
+    Q = rng.standard_normal((r, d))
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d)) * 3
+    last = np.array([-1, 0, 1, 2, 3, 4, 5, 6, 6])
+    O, M2 = oracle.causal_rows(Q, K, V, last, 0.7, moments=True)
+    for i in range(r):
+        if last[i] < 0:
+            assert not O[i].any() and not M2[i].any()
+            continue
+        zs = [0.7 * sum(Q[i, k] * K[t, k] for k in range(d)) for t in range(last[i] + 1)]
+        es = [math.exp(z) for z in zs]
+        w = [e / sum(es) for e in es]
+        for e in range(d):
+            o = sum(w[t] * V[t, e] for t in range(len(w)))
+            m2 = sum(w[t] * V[t, e] ** 2 for t in range(len(w)))
+            mad = sum(w[t] * abs(V[t, e] - o) for t in range(len(w)))
+            assert abs(O[i, e] - o) <= 1e-12 and abs(M2[i, e] - m2) <= 1e-12
+            assert mad <= math.sqrt(max(m2 - o * o, 0.0)) + 1e-12
+    # one visible token: the mean is that value and the spread is zero
+    assert np.allclose(M2[1], V[0] ** 2, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [pin_widening, pin_layout, pin_slot_enumeration, pin_cache_round_trip,
             pin_cache_write_footprint, pin_copy_blocks, pin_sdpa, pin_closed_forms,
             pin_paging_invariance, pin_block_size_invariance, pin_sharing_invariance,
-            pin_poison_ignored, pin_blockwise_online, pin_split_merge, pin_prefill_sdpa,
-            pin_prefill_decode_and_chunks, pin_prefill_longer_than_context, pin_swap_blocks]
+            pin_poison_ignored, pin_blocked_form, pin_split_merge, pin_prefill_sdpa,
+            pin_prefill_decode_and_chunks, pin_prefill_longer_than_context, pin_swap_blocks, pin_causal_moments]

@@ -143,24 +143,53 @@ def m_merge_no_rescale_l(mp):
     _patch(mp, "merge_partition_states_ref", f)
 
 
-def m_online_no_rescale(mp):
+def m_blocked_per_block_denominator(mp):
+    """Each block's weight vector divided by its own block's sum (a misreading of the blocked
+    denominator) instead of the sum over all blocks."""
     def f(q, k_pool, v_pool, row, ctx, scale, g, *, dtype, num_kv_heads, block_size, head_dim):
         scale64 = float(np.float32(scale))
-        out = np.zeros(head_dim); denom = 0.0; mx = -np.inf
+        out = np.zeros(head_dim)
         for j in range(-(-int(ctx) // block_size)):
             valid = min(block_size, int(ctx) - j * block_size)
             K, V = pa_mod.token_kv(k_pool, v_pool, np.full(valid, int(row[j])), np.arange(valid),
                                    dtype=dtype, num_kv_heads=num_kv_heads,
                                    block_size=block_size, head_dim=head_dim)
-            s = scale64 * (K[:, g] @ q)
-            new = max(mx, float(s.max()))
-            c = np.exp(mx - new)
-            p = np.exp(s - new)
-            denom = denom * c + p.sum()
-            out = out + p @ V[:, g]
-            mx = new
-        return out / denom
-    _patch(mp, "blockwise_online_ref", f)
+            z = scale64 * (K[:, g] @ q)
+            e = np.exp(z - z.max())
+            out = out + V[:, g].T @ (e / e.sum())
+        return out
+    _patch(mp, "blocked_form_ref", f)
+
+
+def _causal_with(mp, *, strict=False, scale_factor=1.0):
+    """causal_rows with the query's own token masked out (strict) or the scale changed."""
+    orig = _orig["causal_rows"]
+
+    def f(Q, K, V, last, scale, moments=False):
+        last = np.asarray(last) - (1 if strict else 0)
+        return orig(Q, K, V, last, scale * scale_factor, moments)
+    _patch(mp, "causal_rows", f)
+
+
+def m_causal_excludes_self(mp):
+    _causal_with(mp, strict=True)
+
+
+def m_causal_wrong_scale(mp):
+    _causal_with(mp, scale_factor=0.125)
+
+
+def m_moments_first_moment(mp):
+    """The prefill bound's second moment computed as sum w |v| (a first moment) instead."""
+    orig = _orig["causal_rows"]
+
+    def f(Q, K, V, last, scale, moments=False):
+        if not moments:
+            return orig(Q, K, V, last, scale)
+        O, _ = orig(Q, K, V, last, scale, True)
+        _, M1 = orig(Q, K, np.sqrt(np.abs(V)), last, scale, True)
+        return O, M1
+    _patch(mp, "causal_rows", f)
 
 
 def m_bf16_shift(mp):
@@ -216,8 +245,9 @@ def m_swap_reads_destination_pool(mp):
 MUTATIONS = [m_exp_sign, m_denominator, m_keys_as_values, m_no_scale, m_scale_twice,
              m_head_modulo, m_gather_block_index, m_gather_slot_index, m_gather_one_past,
              m_k_offset_swapped, m_v_offset_transposed, m_slot_swapped, m_copy_only_keys,
-             m_merge_no_rescale_l, m_online_no_rescale, m_bf16_shift, m_prefill_sees_next_token,
-             m_prefill_ignores_chunk_offset, m_swap_reads_destination_pool]
+             m_merge_no_rescale_l, m_blocked_per_block_denominator, m_bf16_shift, m_prefill_sees_next_token,
+             m_prefill_ignores_chunk_offset, m_swap_reads_destination_pool,
+             m_moments_first_moment, m_causal_excludes_self, m_causal_wrong_scale]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__ for m in MUTATIONS])
