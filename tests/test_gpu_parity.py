@@ -3,7 +3,6 @@ oracle to check every output: several tiles, ragged tails, split and unsplit par
 dtype / head_dim / query-group shape, empty contexts and exact block and partition boundaries.
 Cache writes and copies are bit-exact over the whole pools; attention within 1e-5 (fp32) and
 1e-2 (fp16, bf16)."""
-import numpy as np
 import pytest
 
 from paged_kv_cache_384_amd import workloads as wl
@@ -89,14 +88,12 @@ def test_very_long_contexts():
 
 def test_many_short_sequences():
     """4096 sequences of 1-64 tokens (8192 workgroups of mostly one or two blocks), GQA fp16;
-    the oracle checks a sample of 64 sequences, first and last included."""
+    every sequence and head."""
     cfg = wl.DecodeConfig("many_short_f16", "f16", num_seqs=4096, num_q_heads=8, num_kv_heads=2,
                           head_dim=128, ctx=("uniform", 1, 64), seed=41)
-    rng = np.random.default_rng(3)
-    sample = sorted({0, cfg.num_seqs - 1} | set(rng.choice(cfg.num_seqs, 62, replace=False).tolist()))
-    log(f"[parity] many short sequences: {cfg.num_seqs} seqs, sample {len(sample)}")
-    r = run_step(cfg, sample=sample)
-    log(f"    max_abs_err={r['max_abs_err']:.3g}")
+    log(f"[parity] many short sequences: {cfg.num_seqs} seqs")
+    r = run_step(cfg)
+    log(f"    max_abs_err={r['max_abs_err']:.3g} oracle {r['oracle_s']:.1f}s")
 
 
 def test_all_empty():

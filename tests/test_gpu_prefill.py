@@ -3,13 +3,13 @@ cache) with the CPU oracle, through the C ABI.
 
 Each case runs a whole prefill step: the new tokens' keys and values are written with
 pa_reshape_and_cache (pools compared bit for bit), then pa_prefill is compared with
-oracle.paged_prefill_ref query by query within the 16-bit tolerance (1e-2 max abs, on top of
-the half unit in the last place that rounding the exact result to the output type costs). Slots past
+oracle.paged_prefill_ref element by element: within the 16-bit tolerance (1e-2 max abs; plus half
+a unit in the last place only where that half unit itself reaches 1e-2) and within the bound the
+kernel's arithmetic (16-bit softmax weights, fp32 sums, output rounding) guarantees. Slots past
 each context in its last block hold NaN, so a read past the end shows up. The small cases check
 every query; they span several 128-query tiles and 64-token key tiles with ragged tails, GQA and
 MHA, head_dim 64 and 128, block sizes 8/16/32, prompts (every token new) and chunks on top of an
-earlier context. The full-size workloads check a sample of queries, including the first and last
-of the longest sequence.
+earlier context. The full-size workloads check every query of every sequence.
 """
 import numpy as np
 import pytest
@@ -18,7 +18,7 @@ import torch
 import paged_kv_cache_384_amd as pa
 from paged_kv_cache_384_amd import workloads as wl
 import oracle
-from _gpu_cases import Prepared, excess_error, log, run_prefill
+from _gpu_cases import Prepared, check_prefill, log, run_prefill
 from _helpers import to_storage
 
 pytestmark = pytest.mark.gpu
@@ -50,8 +50,8 @@ CASES = [
 def test_prefill_small(cfg):
     log(f"[prefill] {cfg.name}: ctx={cfg.ctx} new={cfg.new_tokens}")
     r = run_prefill(cfg)
-    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} beyond output rounding "
-        f"{r['excess_err']:.3g} max|o|={r['max_abs_out']:.3g}")
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} "
+        f"max err/bound={r['max_err_over_bound']:.3g} max|o|={r['max_abs_out']:.3g}")
 
 
 def test_prefill_max_query_len_truncates():
@@ -92,16 +92,13 @@ def test_prefill_chunk_longer_than_context():
                   b.max_context_len)
     torch.cuda.synchronize()
     out = to_storage(out_d)
-    ref = oracle.paged_prefill_ref(P.q, P.kp, P.vp, b.block_tables, b.query_start, ctx2,
-                                   cfg.scale, **P.kw)
-    worst = 0.0
-    for (s, j), r in ref.items():
-        got = oracle.to_f64(out[int(b.query_start[s]) + j], cfg.dtype)
-        if int(ctx2[s]) - int(b.query_lens[s]) + j < 0:
-            assert np.array_equal(got, np.zeros_like(got)), (s, j)
-        worst = max(worst, excess_error(got, r, cfg.dtype))
-    log(f"    {len(ref)} rows, error beyond output rounding {worst:.3g}")
-    assert worst <= 1e-2
+    for s in (0, 2):
+        for j in range(int(b.query_lens[s]) - int(ctx2[s])):
+            row = oracle.to_f64(out[int(b.query_start[s]) + j], cfg.dtype)
+            assert np.array_equal(row, np.zeros_like(row)), (s, j)
+    rows = {s: list(range(int(b.query_lens[s]))) for s in range(cfg.num_seqs)}
+    r = check_prefill(P, out, rows, ctx2, cfg.name)
+    log(f"    {r['rows']} rows, max abs error {r['max_abs_err']:.3g}")
 
 
 def test_prefill_empty_sequences_and_zero_len():
@@ -121,51 +118,38 @@ def test_prefill_empty_sequences_and_zero_len():
 
 def test_prefill_long_context_chunks():
     """Chunks on top of 16K-20K-token contexts (several hundred key/value tiles per workgroup,
-    block tables of hundreds of entries), bf16 GQA at B = 32; sampled queries of every sequence,
-    first and last included."""
+    block tables of hundreds of entries), bf16 GQA at B = 32; every query of every sequence."""
     cfg = small("long_chunk_bf16", "bf16", 3, 8, 2, 128, 32, ("uniform", 16000, 20000),
                 ("uniform", 200, 300), 19)
     P = Prepared(cfg, device_values=True)
-    ql = P.batch.query_lens
-    rng = np.random.default_rng(7)
-    rows = {s: sorted({0, int(ql[s]) - 1} | set(rng.integers(0, ql[s], 6).tolist()))
-            for s in range(cfg.num_seqs)}
-    log(f"[prefill] long chunks ctx={P.batch.context_lens.tolist()} q={ql.tolist()}")
-    r = run_prefill(cfg, rows=rows, prepared=P)
-    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} beyond output rounding "
-        f"{r['excess_err']:.3g}")
+    log(f"[prefill] long chunks ctx={P.batch.context_lens.tolist()} "
+        f"q={P.batch.query_lens.tolist()}")
+    r = run_prefill(cfg, prepared=P)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} "
+        f"max err/bound={r['max_err_over_bound']:.3g}")
 
 
+@pytest.mark.timeout(600)
 def test_prefill_long_prompts():
     """Whole prompts of 8192 and 5000 tokens (64 and 40 query tiles per sequence, tile-major
-    units), bf16 GQA at B = 16: sampled queries on both sides of tile edges, first and last."""
+    units), bf16 GQA at B = 16: every query of both prompts."""
     cfg = small("long_prompt_bf16", "bf16", 2, 8, 2, 128, 16, ("fixed", (8192, 5000)), ("all",), 24)
     P = Prepared(cfg, device_values=True)
-    ql = P.batch.query_lens
-    rng = np.random.default_rng(9)
-    rows = {s: sorted({0, 1, 63, 64, 127, 128, int(ql[s]) // 2, int(ql[s]) - 1} |
-                      set(rng.integers(0, ql[s], 8).tolist())) for s in range(cfg.num_seqs)}
-    log(f"[prefill] long prompts q={ql.tolist()}")
-    r = run_prefill(cfg, rows=rows, prepared=P)
-    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} beyond output rounding "
-        f"{r['excess_err']:.3g}")
+    log(f"[prefill] long prompts q={P.batch.query_lens.tolist()}")
+    r = run_prefill(cfg, prepared=P)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} "
+        f"max err/bound={r['max_err_over_bound']:.3g} oracle {r['oracle_s']:.1f}s")
 
 
 @pytest.mark.parametrize("name", ["prefill_bf16", "chunked_fp16"])
 @pytest.mark.timeout(900)
 def test_prefill_full_size(name):
+    """Both prefill workloads at full size, every query row of every sequence and head."""
     cfg = wl.PREFILL_CONFIGS[name]
     P = Prepared(cfg, device_values=True)
-    b = P.batch
-    ql = b.query_lens
-    rng = np.random.default_rng(5)
-    longest = int(np.argmax(ql))
-    rows = {longest: sorted({0, 1, int(ql[longest]) - 1, int(ql[longest]) // 2} |
-                            set(rng.integers(0, ql[longest], 12).tolist()))}
-    for s in rng.choice(cfg.num_seqs, 4, replace=False).tolist():
-        rows.setdefault(s, [])
-        rows[s] = sorted(set(rows[s]) | set(rng.integers(0, ql[s], 8).tolist()) | {int(ql[s]) - 1})
-    log(f"[prefill full] {name}: {sum(len(v) for v in rows.values())} sampled rows")
-    r = run_prefill(cfg, rows=rows, prepared=P)
-    log(f"    max_abs_err={r['max_abs_err']:.3g} max|o|={r['max_abs_out']:.3g} "
-        f"oracle {r['oracle_s']:.1f}s")
+    log(f"[prefill full] {name}: every one of {int(P.batch.query_lens.sum())} query rows")
+    r = run_prefill(cfg, prepared=P)
+    log(f"    rows={r['rows']} max_abs_err={r['max_abs_err']:.3g} "
+        f"max err/bar={r['max_err_over_bar']:.3g} max err/bound={r['max_err_over_bound']:.3g} "
+        f"bound>tol elements={r['bound_over_tol_elems']} of {r['elements']} "
+        f"max|o|={r['max_abs_out']:.3g} oracle {r['oracle_s']:.1f}s")
