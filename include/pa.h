@@ -3,8 +3,9 @@
  *
  * Plain C ABI: raw pointers and sizes, no HIP or PyTorch types. Streams are hipStream_t
  * handles passed as void* (NULL = the default stream). All device buffers are owned by the
- * caller; the library allocates no device memory and keeps no per-call state. Every call is
- * asynchronous on its stream.
+ * caller; the library allocates no device memory and keeps no per-call state (the one exception
+ * is pa_decode_static's fixed partition-state array, which the library holds on each device
+ * from its loading on). Every call is asynchronous on its stream.
  *
  * Sources, cited by page title and section:
  *   [wiki] "PagedAttention" (newikis.com/ko/PagedAttention), "수학적 공식" (mathematical
@@ -62,7 +63,7 @@ extern "C" {
 #define PA_API
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -173,6 +174,31 @@ PA_API pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const 
                     int32_t num_q_heads, float scale, int32_t max_context_len,
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * pa_decode_static — pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The partition states
+ * live in a fixed device array of PA_STATIC_WORKSPACE_BYTES that the library itself holds on
+ * every GPU it runs on (from the library's loading until the process ends) instead of in a
+ * caller's workspace; the call allocates nothing.
+ *
+ * Arguments, results, checks and kernels are pa_decode's, without workspace / workspace_bytes.
+ * Sizes for which pa_decode_workspace_bytes(...) exceeds PA_STATIC_WORKSPACE_BYTES give
+ * PA_ERR_WORKSPACE, checked on the host before any HIP call. The call uses the array of the
+ * calling thread's current device, and `stream` must belong to that device. Every call on one
+ * device shares that device's array, which keeps the last call's partition states: calls that
+ * overlap on one device (on two streams, or from two threads, at once) race, and the caller
+ * must order them. The contents need no clearing (every partition state is written before it
+ * is read). The array's device address is looked up once per device, on the first call that
+ * needs it (hipGetSymbolAddress); a failed lookup gives PA_ERR_LAUNCH.
+ */
+#define PA_STATIC_WORKSPACE_BYTES (32u * 1024u * 1024u)
+PA_API pa_status pa_decode_static(const pa_cache_desc* c, const void* key_cache,
+                                  const void* value_cache, void* out, const void* query,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, int32_t max_context_len,
+                                  int32_t partition_size, void* stream);
 
 /*
  * The two stages pa_decode launches, exported separately (same arguments, same checks) so a

@@ -8,6 +8,8 @@ kernels; there is no fallback. If the library is not built, the first call raise
     pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token_seq, token_pos)
     pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
               max_context_len, partition_size=0, workspace=None)
+    pa_decode_static(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     max_context_len, partition_size=0)        # allocates nothing
     pa_prefill(out, query, key_cache, value_cache, block_tables, query_start, context_lens,
                scale, max_query_len, max_context_len)
     pa_copy_blocks(key_cache, value_cache, src_dst)
@@ -22,19 +24,22 @@ import ctypes
 import os
 
 __all__ = [
-    "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_attention",
+    "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_static",
+    "pa_decode_attention", "STATIC_WORKSPACE_BYTES",
     "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks",
     "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_validate_tables", "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
+STATIC_WORKSPACE_BYTES = 32 * 1024 * 1024  # PA_STATIC_WORKSPACE_BYTES
 CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
+                    "pa_decode_static",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
                     "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_validate_tables",
                     "pa_status_string", "pa_abi_version"]
@@ -77,6 +82,8 @@ def lib() -> ctypes.CDLL:
         for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
             getattr(L, name).argtypes = _DECODE_ARGS
             getattr(L, name).restype = ctypes.c_int
+        L.pa_decode_static.argtypes = _DECODE_ARGS[:13] + [_vp]
+        L.pa_decode_static.restype = ctypes.c_int
         L.pa_decode_contiguous.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                            ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t, _vp]
         L.pa_decode_contiguous.restype = ctypes.c_int
@@ -228,6 +235,30 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     return _decode_call("pa_decode", out, query, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, partition_size, workspace,
                         block_size, shared_blocks, stream)
+
+
+def pa_decode_static(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                     max_context_len, partition_size: int = 0, *, block_size: int | None = None,
+                     shared_blocks: bool = False, stream=None) -> None:
+    """pa_decode with the partition states in the library's own fixed device array
+    (STATIC_WORKSPACE_BYTES per GPU) instead of a workspace: allocates nothing. Calls that
+    overlap on one GPU share that array and must be ordered by the caller."""
+    import torch
+    S, Hq, head_dim = query.shape
+    d = _desc(key_cache, head_dim, block_size, shared_blocks)
+    if out.shape != query.shape or out.dtype != query.dtype:
+        raise ValueError("out must match query in shape and dtype")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key and value pools differ in shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]; context_lens [num_seqs]")
+    args = (ctypes.byref(d), _dev(key_cache, "key_cache", query.dtype),
+            _dev(value_cache, "value_cache", query.dtype), _dev(out, "out"),
+            _dev(query, "query"), _dev(block_tables, "block_tables", torch.int32),
+            block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S, Hq,
+            float(scale), int(max_context_len), int(partition_size), _stream(query, stream))
+    with torch.cuda.device(query.device):  # the library uses the current device's array
+        _check(lib().pa_decode_static(*args), "pa_decode_static")
 
 
 def pa_decode_attention(out, query, key_cache, value_cache, block_tables, context_lens, scale,

@@ -1,15 +1,50 @@
 // C ABI of the paged attention library: argument checks on the host, partition choice, dispatch.
-// Every check runs before any launch; besides the launches and hipGetLastError the only HIP call
-// is pa_swap_blocks' pointer query (hipPointerGetAttributes). No device memory is allocated.
+// Every check runs before any launch; besides the launches and hipGetLastError the only HIP calls
+// are pa_swap_blocks' pointer query (hipPointerGetAttributes) and pa_decode_static's one-time
+// lookup of its device array (hipGetDevice, hipGetSymbolAddress). No device memory is allocated.
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "pa_kernels.h"
 
+// pa_decode_static's partition-state array. Each GPU the library runs on holds its own copy
+// (at its own address) until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address scratch_address() looked up for the current device.
+static __device__ __align__(256) uint8_t scratch[PA_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 using pa::DType;
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the calling thread's current device, looked up once per
+// device (with that device current); nullptr if the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 constexpr int kStageAttention = 1;
 constexpr int kStageReduce = 2;
@@ -90,12 +125,15 @@ pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_he
 
 // paged = false: the contiguous twin (no table; sequence s's block j is physical block
 // s * max_blocks_per_seq + j), block_tables unused.
+// use_static: the partition states go to the library's own device array (pa_decode_static)
+// instead of the caller's workspace.
 pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void* key_cache,
                       const void* value_cache, void* out, const void* query,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                       float scale, int32_t max_context_len, int32_t partition_size,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      bool use_static = false) {
   DecodePlan plan;
   pa_status st = plan_decode(c, num_seqs, num_q_heads, max_context_len, partition_size, &plan);
   if (st != PA_OK) return st;
@@ -113,9 +151,15 @@ pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(out, 16) ||
       !aligned(query, 16) || (paged && !aligned(block_tables, 4)) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
-  if (plan.workspace_bytes > 0) {
+  if (use_static && plan.workspace_bytes > PA_STATIC_WORKSPACE_BYTES) return PA_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !use_static) {
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  }
+  if (plan.workspace_bytes > 0 && use_static) {
+    workspace = scratch_address();
+    if (workspace == nullptr) return PA_ERR_LAUNCH;
+    workspace_bytes = PA_STATIC_WORKSPACE_BYTES;
   }
 
   pa::DecodeArgs a;
@@ -237,6 +281,17 @@ pa_status pa_decode(const pa_cache_desc* c, const void* key_cache, const void* v
   return decode_impl(kStageAttention | kStageReduce, true, c, key_cache, value_cache, out, query,
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
                      max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_static(const pa_cache_desc* c, const void* key_cache,
+                           const void* value_cache, void* out, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, int32_t max_context_len, int32_t partition_size,
+                           void* stream) {
+  return decode_impl(kStageAttention | kStageReduce, true, c, key_cache, value_cache, out, query,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                     max_context_len, partition_size, nullptr, 0, stream, true);
 }
 
 pa_status pa_decode_attention(const pa_cache_desc* c, const void* key_cache,

@@ -113,6 +113,35 @@ def test_stage_entry_points_share_validation(L):
                   32, P(0), 0, P(0)) == WS
 
 
+def test_static_decode_validation(L):
+    """pa_decode_static makes pa_decode's checks, and refuses sizes whose partition states
+    exceed its fixed array (PA_ERR_WORKSPACE), all before any HIP call."""
+    def ds(d=None, *, S=2, Hq=4, maxb=8, max_ctx=100, part=0, ptrs=None):
+        d = desc() if d is None else d
+        p = ptrs or {}
+        return L.pa_decode_static(ctypes.byref(d) if d is not False else None,
+                                  p.get("k", GOOD), p.get("v", GOOD), p.get("out", GOOD),
+                                  p.get("q", GOOD), p.get("bt", GOOD), maxb, p.get("ctx", GOOD),
+                                  S, Hq, 0.1, max_ctx, part, P(0))
+    assert ds(False) == NULL
+    assert ds(desc(d=96)) == UNSUP
+    assert ds(Hq=6) == SHAPE
+    assert ds(part=24) == SHAPE
+    assert ds(max_ctx=8 * 16 + 1) == SHAPE
+    for k in ("k", "v", "out", "q", "bt", "ctx"):
+        assert ds(ptrs={k: P(0)}) == NULL, k
+    assert ds(ptrs={"q": ODD}) == ALIGN
+    assert ds(S=0, ptrs={k: P(0) for k in ("k", "v", "out", "q", "bt", "ctx")}) == OK
+    # 2 x 64 heads x 513 partitions of (128 + 2) floats = 34 145 280 bytes > 32 MiB
+    big = dict(S=2, Hq=64, maxb=1024, max_ctx=8200, part=16)
+    d8 = desc(hkv=8, nb=4096)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d8), 2, 64, 8200, 16) > pa.STATIC_WORKSPACE_BYTES
+    assert ds(d8, **big) == WS
+    # at 32-token partitions the same batch needs half that: it passes every host check (so
+    # it is not run here, where it would launch)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d8), 2, 64, 8200, 32) <= pa.STATIC_WORKSPACE_BYTES
+
+
 def test_contiguous_twin_validation(L):
     def dc(d=None, *, S=2, maxb=8, max_ctx=100, ptrs=None):
         d = desc() if d is None else d
