@@ -63,7 +63,7 @@ extern "C" {
 #define PA_API
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -71,7 +71,8 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
-  PA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent (this includes
+                             sizes whose launch would exceed 2^32 - 1 work-items) */
   PA_ERR_UNSUPPORTED = 3, /* dtype, head_dim, block_size or flag the kernels do not support, or
                              memory the device cannot address (pa_swap_blocks) */
   PA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned (int arrays: 4-byte) */
@@ -116,10 +117,11 @@ typedef struct {
  *   block_tables            device int32 [num_seqs][max_blocks_per_seq], row-major
  *   token_seq, token_pos    device int32 [num_tokens]
  *   num_tokens = 0          returns PA_OK without launching
- * Caller contract (not checked on the device beyond clamping): distinct tokens map to distinct
- * slots; block ids in [0, NB). A token whose sequence is outside [0, num_seqs) or whose position
- * is at or past max_blocks_per_seq * B is skipped; a block id outside [0, NB) is clamped into
- * range (no fault, but the write lands in the wrong block).
+ * Caller contract (not checked on the device beyond clamping; pa_validate_writes counts
+ * violations): distinct tokens map to distinct slots; block ids in [0, NB). A token whose
+ * sequence is outside [0, num_seqs) or whose position is at or past max_blocks_per_seq * B is
+ * skipped; a block id outside [0, NB) is clamped into range (no fault, but the write lands in the
+ * wrong block).
  */
 PA_API pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* value_cache,
                                const void* key, const void* value, const int32_t* block_tables,
@@ -162,7 +164,7 @@ PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs
  *   max_context_len         host-side upper bound of context_lens (sizes the grid; no
  *                           device-to-host copy is made); must be <= max_blocks_per_seq * B.
  *                           A context above it is truncated to it.
- *   workspace               device, >= pa_decode_workspace_bytes(...) bytes, 256-B aligned
+ *   workspace               device, >= pa_decode_workspace_bytes(...) bytes, 16-byte aligned
  *                           (may be NULL when that is 0); contents need no initialisation.
  * Errors: checked on the host before any HIP call (PA_ERR_NULL / SHAPE / UNSUPPORTED / ALIGN /
  * WORKSPACE); a failed launch gives PA_ERR_LAUNCH. num_seqs = 0 returns PA_OK. A block id
@@ -294,8 +296,9 @@ PA_API pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const
  * head and every slot, bit for bit.
  *   src_dst   device int32 [num_pairs][2]
  *   num_pairs = 0 returns PA_OK without launching
- * Caller contract: destination ids are distinct and none is also a source in the same call
- * (otherwise the copies race). A pair with an id outside [0, NB) is skipped.
+ * Caller contract (pa_validate_writes counts violations): destination ids are distinct and none
+ * is also a source in the same call (otherwise the copies race). A pair with an id outside
+ * [0, NB) is skipped.
  */
 PA_API pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_cache,
                          const int32_t* src_dst, int32_t num_pairs, void* stream);
@@ -357,8 +360,40 @@ PA_API pa_status pa_validate_tables(const pa_cache_desc* c, const int32_t* block
                                     const int32_t* context_lens, const int32_t* query_start,
                                     int32_t max_context_len, int32_t* violations, void* stream);
 
-/* Static description of a status code (never NULL). */
-PA_API const char* pa_status_string(pa_status s);
+/*
+ * pa_validate_writes — count violations of the write-race contract of pa_reshape_and_cache and
+ * pa_copy_blocks on the device, without touching the pools.
+ * ([blog] ② and the copy-on-write section of [dev]: a shared block is copied before a sharer
+ *  writes into it precisely so that no two writers ever share a slot; [blog] §2: each new token
+ *  owns one free slot of its sequence's last block.)
+ *
+ * Arguments as pa_reshape_and_cache (block_tables, num_seqs, max_blocks_per_seq, token_seq,
+ * token_pos, num_tokens) and pa_copy_blocks (src_dst, num_pairs) of one step. Counted:
+ *   for each token pa_reshape_and_cache writes (position >= 0, sequence in [0, num_seqs),
+ *   position < max_blocks_per_seq * B):
+ *     one if its table entry block_tables[s][p / B] lies outside [0, c->num_blocks);
+ *     one if its slot (after the clamping that call applies) is also written by an earlier such
+ *     token (k tokens on one slot count k - 1);
+ *   for each pair pa_copy_blocks copies (both ids in [0, c->num_blocks)):
+ *     one if its destination is also the destination of an earlier such pair;
+ *     one if its destination is the source of any such pair, itself included.
+ * The count is written to *violations (device int32, 4-byte aligned), which the library clears
+ * first with a kernel of its own (no memset), so the call can be captured in a graph. The work
+ * is quadratic (num_tokens^2 / 2 + num_pairs^2 comparisons on the device): a checker for tests and
+ * debugging. block_tables / token_seq / token_pos may be NULL when num_tokens = 0, src_dst when
+ * num_pairs = 0; num_tokens + num_pairs must stay below 2^30.
+ * Errors: checked on the host before any launch (PA_ERR_NULL / SHAPE / UNSUPPORTED / ALIGN); a
+ * failed launch gives PA_ERR_LAUNCH.
+ */
+PA_API pa_status pa_validate_writes(const pa_cache_desc* c, const int32_t* block_tables,
+                                    int32_t num_seqs, int32_t max_blocks_per_seq,
+                                    const int32_t* token_seq, const int32_t* token_pos,
+                                    int32_t num_tokens, const int32_t* src_dst, int32_t num_pairs,
+                                    int32_t* violations, void* stream);
+
+/* Static description of a status code (never NULL; "unknown status" for a value that is not a
+ * pa_status). The code is taken as a plain int so that any value a caller passes is defined. */
+PA_API const char* pa_status_string(int status);
 
 /* PA_ABI_VERSION of the built library. */
 PA_API int32_t pa_abi_version(void);

@@ -27,22 +27,24 @@ __all__ = [
     "PaError", "lib", "library_path", "pa_reshape_and_cache", "pa_decode", "pa_decode_static",
     "pa_decode_attention", "STATIC_WORKSPACE_BYTES",
     "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks",
-    "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_validate_tables", "pa_status_string",
+    "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_validate_tables", "pa_validate_writes",
+    "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 STATIC_WORKSPACE_BYTES = 32 * 1024 * 1024  # PA_STATIC_WORKSPACE_BYTES
 CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY selects another build of the same library (e.g. one with host-side sanitizers)
+library_path = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
                     "pa_decode_static",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
                     "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_validate_tables",
-                    "pa_status_string", "pa_abi_version"]
+                    "pa_validate_writes", "pa_status_string", "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -96,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_validate_tables.argtypes = [_desc_p, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
         L.pa_validate_tables.restype = ctypes.c_int
+        L.pa_validate_writes.argtypes = [_desc_p, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32, _vp,
+                                         _vp]
+        L.pa_validate_writes.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
@@ -373,6 +378,40 @@ def pa_validate_tables(key_cache, block_tables, context_lens, max_context_len: i
             int(max_context_len), _dev(violations, "violations", torch.int32),
             _stream(key_cache, stream))
     _check(lib().pa_validate_tables(*args), "pa_validate_tables")
+    return violations
+
+
+def pa_validate_writes(key_cache, violations=None, *, head_dim: int, block_tables=None,
+                       token_seq=None, token_pos=None, src_dst=None, block_size: int | None = None,
+                       stream=None):
+    """Count violations of the write-race contract of one step's pa_reshape_and_cache (tokens
+    given by block_tables, token_seq, token_pos) and pa_copy_blocks (src_dst pairs) into
+    ``violations`` (a GPU int32 tensor of one element, allocated if None), which is returned:
+    table entries outside the pool, slots written twice, destinations written twice or read
+    by a pair of the same call."""
+    import torch
+    d = _desc(key_cache, head_dim, block_size)
+    none = _vp(0)
+    T = 0 if token_seq is None else token_seq.numel()
+    if T:
+        if block_tables is None or block_tables.dim() != 2 or token_pos is None or \
+                token_pos.numel() != T:
+            raise ValueError("tokens need block_tables [num_seqs, max_blocks] and token_pos")
+    npairs = 0 if src_dst is None else src_dst.numel() // 2
+    if src_dst is not None and src_dst.numel() % 2:
+        raise ValueError("src_dst must hold (src, dst) pairs")
+    if violations is None:
+        violations = torch.empty(1, dtype=torch.int32, device=key_cache.device)
+    if violations.numel() != 1:
+        raise ValueError("violations must hold one int32")
+    args = (ctypes.byref(d),
+            _dev(block_tables, "block_tables", torch.int32) if T else none,
+            block_tables.shape[0] if T else 0, block_tables.shape[1] if T else 0,
+            _dev(token_seq, "token_seq", torch.int32) if T else none,
+            _dev(token_pos, "token_pos", torch.int32) if T else none, T,
+            _dev(src_dst, "src_dst", torch.int32) if npairs else none, npairs,
+            _dev(violations, "violations", torch.int32), _stream(key_cache, stream))
+    _check(lib().pa_validate_writes(*args), "pa_validate_writes")
     return violations
 
 

@@ -31,8 +31,28 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source to an object in parallel, then link libpa.so atomically."""
+# Host-side sanitizers (AddressSanitizer, UndefinedBehaviorSanitizer) for the library's host code:
+# the argument checks, planning and launch paths. Device code is compiled as usual. The library
+# built with them leaves the sanitizer runtime unresolved; a process loads it first (LD_PRELOAD of
+# the ASan runtime, which also carries the UBSan handlers).
+HOST_SANITIZE_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                       "-Xarch_host -fno-sanitize-recover=undefined "
+                       "-Xarch_host -fno-omit-frame-pointer -Xarch_host -g").split()
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime shared library of hipcc's clang."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    return out
+
+
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every source to an object in parallel, then link the library (libpa.so unless
+    ``out`` names another path) atomically."""
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
         procs = []
         objs = []
@@ -48,20 +68,20 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             objs.append(obj)
         failed = []
         for src, p in procs:
-            out, _ = p.communicate()
+            log, _ = p.communicate()
             # drop the expected host-side notice about the fp32-packing feature
-            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            lines = [ln for ln in log.splitlines() if "packed-fp32-ops" not in ln]
             if lines and (verbose or p.returncode):
                 print("\n".join(lines), file=sys.stderr)
             if p.returncode:
                 failed.append(src)
         if failed:
             raise RuntimeError(f"hipcc failed for {failed}")
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         subprocess.run(cmd, check=True)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

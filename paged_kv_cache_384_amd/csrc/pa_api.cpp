@@ -49,6 +49,10 @@ void* scratch_address() {
 constexpr int kStageAttention = 1;
 constexpr int kStageReduce = 2;
 
+// A dispatch's grid is at most 2^32 - 1 work-items; every kernel here runs 256-thread
+// workgroups, so a launch may have at most this many of them.
+constexpr int64_t kMaxWorkgroups = ((int64_t{1} << 32) - 1) / 256;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int elem_size(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
@@ -113,7 +117,9 @@ pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_he
   const int32_t part = choose_partition(c, max_context_len, nh, partition_size);
   const int32_t np = max_context_len <= part ? 1 : (max_context_len + part - 1) / part;
   const int64_t wgs = static_cast<int64_t>(c->num_kv_heads) * num_seqs * (group / nh) * np;
-  if (wgs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (wgs > kMaxWorkgroups) return PA_ERR_SHAPE;
+  // the merge runs one workgroup (or one wavefront) per (sequence, query head)
+  if (np > 1 && static_cast<int64_t>(num_seqs) * num_q_heads > kMaxWorkgroups) return PA_ERR_SHAPE;
   plan->part_tokens = part;
   plan->num_parts = np;
   plan->heads_per_wg = nh;
@@ -235,6 +241,7 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* va
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (num_seqs <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * c->block_size > INT32_MAX) return PA_ERR_SHAPE;
   if (!key_cache || !value_cache || !key || !value || !block_tables || !token_seq || !token_pos)
     return PA_ERR_NULL;
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key, 16) ||
@@ -244,7 +251,7 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, void* va
   // one thread per 16-byte piece of every token's heads, 256 per workgroup
   const int64_t pieces = static_cast<int64_t>(num_tokens) * c->num_kv_heads * c->head_dim *
                          elem_size(c->dtype) / 16;
-  if ((pieces + 255) / 256 >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if ((pieces + 255) / 256 > kMaxWorkgroups) return PA_ERR_SHAPE;
   pa::CacheWriteArgs a;
   a.k_pool = static_cast<uint8_t*>(key_cache);
   a.v_pool = static_cast<uint8_t*>(value_cache);
@@ -347,7 +354,7 @@ pa_status pa_prefill(const pa_cache_desc* c, const void* key_cache, const void* 
   const int64_t units = (seq_major ? 1 : tiles) * num_seqs * c->num_kv_heads;
   const int64_t unit_wgs = (seq_major ? tiles : 1) * group;
   const int64_t wgs = (units + 7) / 8 * 8 * unit_wgs;
-  if (wgs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (wgs > kMaxWorkgroups) return PA_ERR_SHAPE;
   if (wgs == 0) return PA_OK;
   if (!key_cache || !value_cache || !out || !query || !block_tables || !query_start ||
       !context_lens)
@@ -401,7 +408,7 @@ pa_status pa_copy_blocks(const pa_cache_desc* c, void* key_cache, void* value_ca
   a.src_num_blocks = a.dst_num_blocks = c->num_blocks;
   a.block_bytes = tile_bytes(c) * c->num_kv_heads;
   const int64_t chunks = (a.block_bytes / 16 + 2047) / 2048;
-  if (chunks * num_pairs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (chunks * num_pairs > kMaxWorkgroups) return PA_ERR_SHAPE;
   if (pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
@@ -418,7 +425,7 @@ pa_status pa_validate_tables(const pa_cache_desc* c, const int32_t* block_tables
       static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
     return PA_ERR_SHAPE;
   if (static_cast<int64_t>(num_seqs) * (static_cast<int64_t>(max_blocks_per_seq) + 3) >=
-      (int64_t{1} << 31))
+      (int64_t{1} << 31) || num_seqs > kMaxWorkgroups)
     return PA_ERR_SHAPE;
   if (!violations) return PA_ERR_NULL;
   if (num_seqs > 0 && (!block_tables || !context_lens)) return PA_ERR_NULL;
@@ -436,6 +443,43 @@ pa_status pa_validate_tables(const pa_cache_desc* c, const int32_t* block_tables
   a.block_size = c->block_size;
   a.max_ctx = max_context_len;
   if (pa::launch_validate(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_validate_writes(const pa_cache_desc* c, const int32_t* block_tables,
+                             int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* token_seq, const int32_t* token_pos,
+                             int32_t num_tokens, const int32_t* src_dst, int32_t num_pairs,
+                             int32_t* violations, void* stream) {
+  pa_status st = check_desc(c);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_pairs < 0) return PA_ERR_SHAPE;
+  // each token counts at most 2, each pair at most 2: the count stays below 2^31
+  if (static_cast<int64_t>(num_tokens) + num_pairs >= (int64_t{1} << 30)) return PA_ERR_SHAPE;
+  if (num_tokens > 0 &&
+      (num_seqs <= 0 || max_blocks_per_seq <= 0 ||
+       static_cast<int64_t>(max_blocks_per_seq) * c->block_size > INT32_MAX))
+    return PA_ERR_SHAPE;
+  if (!violations) return PA_ERR_NULL;
+  if (num_tokens > 0 && (!block_tables || !token_seq || !token_pos)) return PA_ERR_NULL;
+  if (num_pairs > 0 && !src_dst) return PA_ERR_NULL;
+  if (!aligned(violations, 4) || !aligned(block_tables, 4) || !aligned(token_seq, 4) ||
+      !aligned(token_pos, 4) || !aligned(src_dst, 4))
+    return PA_ERR_ALIGN;
+  pa::ValidateWritesArgs a;
+  a.block_tables = block_tables;
+  a.token_seq = token_seq;
+  a.token_pos = token_pos;
+  a.pairs = src_dst;
+  a.violations = violations;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_tokens = num_tokens;
+  a.num_pairs = num_pairs;
+  a.num_blocks = c->num_blocks;
+  a.block_size = c->block_size;
+  if (pa::launch_validate_writes(a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
 }
@@ -467,14 +511,14 @@ pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_valu
   a.dst_num_blocks = dst->num_blocks;
   a.block_bytes = tile_bytes(src) * src->num_kv_heads;
   const int64_t chunks = (a.block_bytes / 16 + 2047) / 2048;
-  if (chunks * num_pairs >= (int64_t{1} << 31)) return PA_ERR_SHAPE;
+  if (chunks * num_pairs > kMaxWorkgroups) return PA_ERR_SHAPE;
   if (pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
 }
 
-const char* pa_status_string(pa_status s) {
-  switch (s) {
+const char* pa_status_string(int status) {
+  switch (status) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";

@@ -148,4 +148,102 @@ hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// pa_validate_writes. Every comparison is one against all: workgroup w holds items
+// [w*256, w*256 + 256) in registers and streams the items it compares them with through LDS, 256
+// at a time, each thread scanning the whole LDS tile (same address in every lane: a broadcast).
+
+// The slot pa_reshape_and_cache writes for token n (the clamped block id times B plus p % B), or
+// -1 when it skips the token; *bad_id is set when the table entry lies outside the pool.
+__device__ int64_t write_slot(const ValidateWritesArgs& a, int n, int* bad_id) {
+  const int s = a.token_seq[n];
+  const int pos = a.token_pos[n];
+  *bad_id = 0;
+  if (pos < 0 || pos >= a.max_blocks * a.block_size || s < 0 || s >= a.num_seqs) return -1;
+  int blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + pos / a.block_size];
+  if (blk < 0 || blk >= a.num_blocks) {
+    *bad_id = 1;
+    blk = blk < 0 ? 0 : a.num_blocks - 1;
+  }
+  return static_cast<int64_t>(blk) * a.block_size + pos % a.block_size;
+}
+
+__device__ void add_count(int32_t* count, int bad) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+  if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(count, bad);
+}
+
+// One thread per written token: a table entry outside the pool, and a slot that an earlier token
+// (lower index) also writes, count one each.
+__global__ __launch_bounds__(kValidateThreads) void validate_slots_kernel(ValidateWritesArgs a) {
+  __shared__ int64_t tile[kValidateThreads];
+  const int i = static_cast<int>(blockIdx.x) * kValidateThreads + static_cast<int>(threadIdx.x);
+  int bad = 0;
+  int64_t mine = -1;
+  if (i < a.num_tokens) mine = write_slot(a, i, &bad);
+  int dup = 0;
+  for (int t = 0; t <= static_cast<int>(blockIdx.x); ++t) {
+    const int j = t * kValidateThreads + static_cast<int>(threadIdx.x);
+    int unused;
+    tile[threadIdx.x] = j < a.num_tokens ? write_slot(a, j, &unused) : -1;
+    __syncthreads();
+    const int earlier = t < static_cast<int>(blockIdx.x) ? kValidateThreads
+                                                         : static_cast<int>(threadIdx.x);
+    if (mine >= 0)
+      for (int k = 0; k < earlier; ++k) dup |= tile[k] == mine ? 1 : 0;
+    __syncthreads();
+  }
+  add_count(a.violations, bad + dup);
+}
+
+// One thread per copy pair with both ids in the pool: a destination that an earlier such pair
+// also writes, and a destination that any such pair (itself included) reads, count one each.
+__global__ __launch_bounds__(kValidateThreads) void validate_pairs_kernel(ValidateWritesArgs a) {
+  __shared__ int2 tile[kValidateThreads];
+  const int i = static_cast<int>(blockIdx.x) * kValidateThreads + static_cast<int>(threadIdx.x);
+  int src = -1, dst = -1;
+  if (i < a.num_pairs) {
+    src = a.pairs[2 * i];
+    dst = a.pairs[2 * i + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) src = dst = -1;
+  }
+  int dup = 0, reads = 0;
+  const int tiles = (a.num_pairs + kValidateThreads - 1) / kValidateThreads;
+  for (int t = 0; t < tiles; ++t) {
+    const int j = t * kValidateThreads + static_cast<int>(threadIdx.x);
+    int2 p = make_int2(-1, -1);
+    if (j < a.num_pairs) {
+      p = make_int2(a.pairs[2 * j], a.pairs[2 * j + 1]);
+      if (p.x < 0 || p.x >= a.num_blocks || p.y < 0 || p.y >= a.num_blocks) p = make_int2(-1, -1);
+    }
+    tile[threadIdx.x] = p;
+    __syncthreads();
+    if (dst >= 0) {
+      const int base = t * kValidateThreads;
+      for (int k = 0; k < kValidateThreads; ++k) {
+        const int2 q = tile[k];
+        dup |= (base + k < i && q.y == dst) ? 1 : 0;
+        reads |= q.x == dst ? 1 : 0;
+      }
+    }
+    __syncthreads();
+  }
+  add_count(a.violations, dup + reads);
+}
+
+hipError_t launch_validate_writes(const ValidateWritesArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(64), 0, stream, a.violations);
+  if (a.num_tokens > 0)
+    hipLaunchKernelGGL(validate_slots_kernel,
+                       dim3(static_cast<unsigned>((a.num_tokens + kValidateThreads - 1) /
+                                                  kValidateThreads)),
+                       dim3(kValidateThreads), 0, stream, a);
+  if (a.num_pairs > 0)
+    hipLaunchKernelGGL(validate_pairs_kernel,
+                       dim3(static_cast<unsigned>((a.num_pairs + kValidateThreads - 1) /
+                                                  kValidateThreads)),
+                       dim3(kValidateThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace pa

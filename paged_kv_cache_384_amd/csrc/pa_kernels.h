@@ -12,6 +12,7 @@ constexpr int kGroupTokens = 16;       // tokens one wave-wide key load covers (
 constexpr int kMaxPartitionTokens = 2048;
 constexpr int kDecodeThreads = 256;    // four 64-lane wavefronts per attention workgroup
 constexpr int kReduceThreads = 256;    // threads of a partition-merge workgroup
+constexpr int kValidateThreads = 256;  // threads of a pa_validate_writes workgroup
 
 struct CacheWriteArgs {
   uint8_t* k_pool;
@@ -53,6 +54,22 @@ struct ValidateArgs {
   int32_t num_blocks;
   int32_t block_size;
   int32_t max_ctx;
+};
+
+// Write-race checks of pa_validate_writes: cache-write tokens (as CacheWriteArgs resolves them)
+// and copy pairs, each compared with the others.
+struct ValidateWritesArgs {
+  const int32_t* block_tables;  // [num_seqs][max_blocks]
+  const int32_t* token_seq;     // [num_tokens]
+  const int32_t* token_pos;     // [num_tokens]
+  const int32_t* pairs;         // [num_pairs][2]
+  int32_t* violations;          // [1]
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t num_tokens;
+  int32_t num_pairs;
+  int32_t num_blocks;
+  int32_t block_size;
 };
 
 // One launch of the attention stage covers every (KV head, sequence, head group, partition).
@@ -120,6 +137,7 @@ hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
                                     const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
+hipError_t launch_validate_writes(const ValidateWritesArgs& a, hipStream_t stream);
 hipError_t launch_decode_attention_b8(DType dt, int head_dim, const DecodeArgs& a,
                                       hipStream_t stream);
 hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs& a,

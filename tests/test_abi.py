@@ -280,7 +280,7 @@ def test_prefill_validation(L):
     assert pf(maxb=0) == SHAPE
     for bad in (0.0, -0.1, float("nan"), float("inf")):
         assert pf(scale=bad) == SHAPE, bad
-    assert pf(S=1 << 20, Hq=1 << 10, mql=1 << 12) == SHAPE  # grid past 2^31 workgroups
+    assert pf(S=1 << 20, Hq=1 << 10, mql=1 << 12) == SHAPE  # grid past 2^32 work-items
     for k in ("k", "v", "out", "q", "bt", "qs", "ctx"):
         assert pf(ptrs={k: P(0)}) == NULL, k
     for k in ("k", "v", "out", "q"):
@@ -339,3 +339,66 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
     with pytest.raises(ValueError, match="on the GPU"):
         pa.pa_decode(torch.empty(2, 4, 128, dtype=torch.bfloat16),
                      torch.zeros(2, 4, 128, dtype=torch.bfloat16), pool, pool, bt, ctx, 0.1, 64)
+
+
+MAX_WGS = ((1 << 32) - 1) // 256   # 256-thread workgroups in a grid of at most 2^32 - 1 items
+
+
+def test_grids_stay_below_2_32_work_items(L):
+    """Every launch's grid (256-thread workgroups) is bounded by 2^32 - 1 work-items on the host:
+    one workgroup past the limit gives PA_ERR_SHAPE; at the limit the shape checks pass (a NULL
+    pointer then stops the call before it could launch)."""
+    one = desc(hkv=1)
+    # decode: one workgroup per (KV head, sequence, head group, partition)
+    assert decode(L, one, S=MAX_WGS + 1, Hq=1) == SHAPE
+    assert decode(L, one, S=MAX_WGS, Hq=1, ptrs={"k": P(0)}) == NULL
+    # the merge: one workgroup or wavefront per (sequence, query head) when contexts split
+    d8 = desc(hkv=8, dtype=2)
+    S = 1 << 19                # 16 S attention workgroups fit, 32 S merged heads do not
+    assert decode(L, d8, S=S, Hq=32, maxb=128, max_ctx=2048, ptrs={"k": P(0)}) == SHAPE
+    assert decode(L, d8, S=S - 1, Hq=32, maxb=128, max_ctx=2048, ptrs={"k": P(0)}) == NULL
+    # cache writes: one thread per 16-byte piece (16 pieces per token at d = 128 fp16, Hkv = 1)
+    T = 16 * MAX_WGS
+    args = lambda t, k: (ctypes.byref(one), GOOD, GOOD, k, GOOD, GOOD, 2, 4, GOOD, GOOD, t, P(0))
+    assert L.pa_reshape_and_cache(*args(T + 16, GOOD)) == SHAPE
+    assert L.pa_reshape_and_cache(*args(T, P(0))) == NULL
+    # copies: one workgroup per 32 KiB chunk of a block (Hkv = 8: one chunk per pair)
+    assert L.pa_copy_blocks(ctypes.byref(desc(hkv=8)), GOOD, GOOD, GOOD, MAX_WGS + 1, P(0)) == SHAPE
+    assert L.pa_copy_blocks(ctypes.byref(desc(hkv=8)), P(0), GOOD, GOOD, MAX_WGS, P(0)) == NULL
+    # prefill: one workgroup per (sequence, KV head) unit and query head, units rounded up to 8
+    pq = lambda S, k: L.pa_prefill(ctypes.byref(one), k, GOOD, GOOD, GOOD, GOOD, 8, GOOD, GOOD,
+                                   S, 1, 0.1, 128, 100, P(0))
+    assert pq(MAX_WGS - 7 + 8, GOOD) == SHAPE
+    assert pq(MAX_WGS - 7, P(0)) == NULL
+    # table validation: one workgroup per sequence
+    vt = lambda S: L.pa_validate_tables(ctypes.byref(desc()), GOOD, S, 1, GOOD, P(0), 16, GOOD,
+                                        P(0))
+    assert vt(MAX_WGS + 1) == SHAPE
+
+
+def test_validate_writes_validation(L):
+    """Sizes, pointers and alignment checked before any launch; token and pair arrays may be NULL
+    when there are none."""
+    def vw(d=None, *, S=2, maxb=4, T=3, npairs=2, ptrs=None):
+        d = desc() if d is None else d
+        p = ptrs or {}
+        return L.pa_validate_writes(ctypes.byref(d) if d is not False else None,
+                                    p.get("bt", GOOD), S, maxb, p.get("seq", GOOD),
+                                    p.get("pos", GOOD), T, p.get("pairs", GOOD), npairs,
+                                    p.get("out", GOOD), P(0))
+    assert vw(False) == NULL
+    assert vw(desc(d=96)) == UNSUP
+    assert vw(desc(b=4)) == UNSUP
+    assert vw(T=-1) == SHAPE
+    assert vw(npairs=-1) == SHAPE
+    assert vw(T=1 << 29, npairs=1 << 29) == SHAPE           # the count could overflow
+    assert vw(S=0) == SHAPE
+    assert vw(maxb=0) == SHAPE
+    assert vw(maxb=1 << 27, ptrs={"out": P(0)}) == SHAPE     # positions past int32 (B = 16)
+    for k in ("bt", "seq", "pos", "pairs", "out"):
+        assert vw(ptrs={k: P(0)}) == NULL, k
+    for k in ("bt", "seq", "pos", "pairs", "out"):
+        assert vw(ptrs={k: P(0x10002)}) == ALIGN, k
+    # nothing to compare: only the count's pointer is needed (a launch follows, so stop it there)
+    none = {k: P(0) for k in ("bt", "seq", "pos", "pairs", "out")}
+    assert vw(T=0, npairs=0, S=0, maxb=0, ptrs=none) == NULL
