@@ -1,26 +1,31 @@
 """Benchmark of the paged decode path on one MI355X.
 
 A step is one pass of the whole path over one synthetic decode batch: copy-on-write block
-copies (none in the OPT-13B-shape batch), the cache write of one new token per sequence, the
+copies (shared-prefix batch only), the cache write of one new token per sequence, the
 per-partition attention kernel and the partition merge. Inputs are resident in HBM before the
 timed region; three independently drawn input sets rotate so that repeated steps are not
 served from the 256 MB Infinity Cache.
 
-Two timed passes of K steps each: an eager pass with HIP events around every kernel (the
-attention kernel's average duration gives ``roofline``), then the timed region proper, where
-the whole step is captured once per input set in a HIP graph and replayed K times (``--eager``
-skips the graph pass and reports the eager step time instead).
+Per decode workload, two timed passes of K steps each: an eager pass with HIP events around
+every kernel (the attention kernel's average duration gives ``roofline``), then the timed region
+proper, where the whole step is captured once per input set in a HIP graph and replayed K times
+(``--eager`` skips the graph pass and reports the eager step time instead). The headline
+workload (``--config``, the OPT-13B-shape batch) gives the top-level fields; the other decode
+workloads (``--also``: GQA, long-context, shared-prefix, tiny) are measured in the same run and
+reported under ``workloads`` with the same fields.
 
 Prints one JSON line. ``value`` is KV bytes read per step / step time (GB/s, whole step);
 ``roofline`` reports the attention kernel alone (HIP events on its stream) against the 8 TB/s
-HBM peak; ``hbm_copy_gbps`` is a plain 1 GiB device copy on the same GPU (``frac_of_copy`` =
-value / that); ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
+HBM peak (for batches that share blocks, against the bytes of the distinct blocks);
+``hbm_copy_gbps`` is a plain 1 GiB device copy on the same GPU (``frac_of_copy`` = value /
+that); ``cpu_baseline`` times the CPU oracle on every host core (at most 16 worker processes)
+over the whole batch, with the one-thread figure on a bounded sample beside it.
 
 ``prefill`` (default: the GQA prompt workload) times pa_prefill on a prefill batch and reports
 it against the 16-bit matrix-core peak, with its own CPU-oracle sample.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--partition P] [--eager]
-                    [--prefill NAMES] [--prefill-only]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--also NAMES] [--partition P]
+                    [--eager] [--prefill NAMES] [--prefill-only]
 """
 from __future__ import annotations
 
@@ -74,7 +79,6 @@ def host_storage(t):
 
 def cpu_baseline(batch, host, budget_s: float):
     """The CPU oracle, single-threaded, on as many whole sequences as fit in ``budget_s``."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -97,6 +101,102 @@ def cpu_baseline(batch, host, budget_s: float):
             "sample": f"{done} of {cfg.num_seqs} sequences (all {cfg.num_q_heads} query heads), "
                       f"{kv / 1e6:.1f} MB of KV in {dt:.1f} s, numpy float64, 1 thread",
             "seconds": round(dt, 2), "tokens_per_s": round(done / dt, 3)}
+
+
+# ---- the oracle on every host core: spawned worker processes over shared memory ----------
+# The workers are fresh interpreters (they never touch the GPU); the pools, query and tables are
+# copied once into shared memory, each worker maps them and runs the oracle on groups of whole
+# sequences with one BLAS thread.
+
+_WORKER = {}
+
+
+def _oracle_worker_init(spec):
+    import numpy as np
+    from multiprocessing import shared_memory
+    from threadpoolctl import threadpool_limits
+    _WORKER["limits"] = threadpool_limits(limits=1)
+    _WORKER["shm"] = []
+    arrays = {}
+    for name, (shm_name, shape, dtype) in spec["arrays"].items():
+        # attaching registers the name with the parent's resource tracker again (the spawned
+        # workers share it), which is harmless: the parent unlinks the segments once at the end
+        shm = shared_memory.SharedMemory(name=shm_name)
+        _WORKER["shm"].append(shm)
+        arrays[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
+    _WORKER["arrays"] = arrays
+    _WORKER["meta"] = spec["meta"]
+
+
+def _oracle_worker_run(seqs):
+    import oracle
+    a, m = _WORKER["arrays"], _WORKER["meta"]
+    t0 = time.perf_counter()
+    if seqs:
+        oracle.paged_decode_ref(a["query"], a["k_pool"], a["v_pool"], a["block_tables"],
+                                a["context_lens"], m["scale"], seqs=seqs, dtype=m["dtype"],
+                                num_kv_heads=m["num_kv_heads"], block_size=m["block_size"],
+                                head_dim=m["head_dim"])
+    return time.perf_counter() - t0
+
+
+def host_workers() -> int:
+    """Host cores this process may use, at most 16 (the host share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline_all_cores(batch, host, workers: int):
+    """The CPU oracle over the whole batch on ``workers`` processes (one BLAS thread each), timed
+    from the moment the sequence groups are handed out (workers started and inputs in shared
+    memory already) to the last result."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from multiprocessing import shared_memory
+
+    import numpy as np
+    cfg = batch.cfg
+    arrays = {"query": host["query"], "k_pool": host["k_pool"], "v_pool": host["v_pool"],
+              "block_tables": batch.block_tables, "context_lens": batch.context_lens}
+    segs, spec = [], {"arrays": {}, "meta": dict(scale=float(cfg.scale), dtype=cfg.dtype,
+                                                 num_kv_heads=cfg.num_kv_heads,
+                                                 block_size=cfg.block_size,
+                                                 head_dim=cfg.head_dim)}
+    try:
+        for name, arr in arrays.items():
+            arr = np.ascontiguousarray(arr)
+            shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+            segs.append(shm)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+            spec["arrays"][name] = (shm.name, arr.shape, arr.dtype.str)
+        # groups of whole sequences of similar total length, heaviest first
+        lens = batch.context_lens.astype(np.int64)
+        order = np.argsort(-lens, kind="stable")
+        n_groups = min(cfg.num_seqs, 4 * workers)
+        groups = [[] for _ in range(n_groups)]
+        load = np.zeros(n_groups, np.int64)
+        for s in order.tolist():
+            g = int(np.argmin(load))
+            groups[g].append(s)
+            load[g] += lens[s] + 1
+        groups.sort(key=lambda g: -sum(int(lens[s]) for s in g))
+        # a worker that dies makes the pool raise (BrokenProcessPool) instead of restarting it
+        with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                 initializer=_oracle_worker_init, initargs=(spec,)) as pool:
+            list(pool.map(_oracle_worker_run, [[]] * workers))   # workers up and mapped
+            t0 = time.perf_counter()
+            busy = list(pool.map(_oracle_worker_run, groups))
+            dt = time.perf_counter() - t0
+    finally:
+        for shm in segs:
+            shm.close()
+            shm.unlink()
+    kv = batch.kv_bytes()
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {cfg.num_seqs} sequences (all {cfg.num_q_heads} query heads), "
+                      f"{kv / 1e6:.1f} MB of KV in {dt:.2f} s, numpy float64, {workers} worker "
+                      f"processes of one thread each (cores from sched_getaffinity, at most 16)",
+            "seconds": round(dt, 3), "cpu_seconds": round(float(sum(busy)), 2),
+            "tokens_per_s": round(cfg.num_seqs / dt, 3)}
 
 
 def paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream):
@@ -335,80 +435,25 @@ def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0, **overrides):
             "cpu_baseline": cpu}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="opt13b_fp16")
-    ap.add_argument("--partition", type=int, default=-1,
-                    help="partition size in tokens; -1 = the workload's own setting")
-    ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
-    ap.add_argument("--block-size", type=int, default=0,
-                    help="run the workload at this block size (8, 16 or 32) instead of its own; "
-                         "the pool is then sized for the blocks in use (1.25x)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the eager launches only (no HIP-graph replay of the step)")
-    ap.add_argument("--paging-overhead", action="store_true",
-                    help="also time pa_decode against its contiguous twin (no block table) on a "
-                         "contiguously laid out copy of the batch")
-    ap.add_argument("--swap", action="store_true",
-                    help="also time swapping every block of half the sequences out to pinned "
-                         "host memory and back (pa_swap_blocks)")
-    ap.add_argument("--prefill", default="prefill_bf16",
-                    help="comma-separated prefill workloads to time as well (pa_prefill), e.g. "
-                         "prefill_bf16,chunked_fp16; empty for none")
-    ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the --prefill workloads and print their JSON (--block-size "
-                         "and --placement then apply to them)")
-    ap.add_argument("--placement", default="", choices=["", "shuffled", "contiguous"],
-                    help="with --prefill-only: physical block placement of the prefill batch")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode)", file=sys.stderr)
-        sys.exit(2)
-
+def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=True,
+                paging=False, swap=False):
+    """One decode workload: K eager steps with HIP events around every kernel, then K
+    graph-replayed steps, the CPU oracle (one thread on a bounded sample, and every host core on
+    the whole batch), and the optional paging-overhead and swap measurements. Returns the
+    workload's figures (the headline line is built from the first workload's)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_384_amd as pa
     from paged_kv_cache_384_amd import workloads as wl
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    prefill_names = [n for n in args.prefill.split(",") if n]
-    if args.prefill_only:
-        stream = torch.cuda.current_stream(dev)
-        budget = 0.0 if args.no_cpu_baseline else 5.0
-        over = {}
-        if args.block_size:
-            over.update(block_size=args.block_size, num_blocks=0)
-        if args.placement:
-            over.update(placement=args.placement)
-        res = [prefill_rate(n, args.steps, args.warmup, stream, budget, **over)
-               for n in prefill_names]
-        if args.copy_calibration:
-            copy_calibration(dev)
-        print(json.dumps({"prefill": res}), flush=True)
-        return
-    cfg = wl.CONFIGS[args.config]
-    if args.block_size and args.block_size != cfg.block_size:
-        cfg = wl.config(args.config, block_size=args.block_size, num_blocks=0)
-    part = cfg.partition_size if args.partition < 0 else args.partition
+    cfg = wl.CONFIGS[name]
+    if block_size and block_size != cfg.block_size:
+        cfg = wl.config(name, block_size=block_size, num_blocks=0)
+    part = cfg.partition_size if part_override < 0 else part_override
     batch = wl.build_batch(cfg)
     print(f"[bench] {cfg.name}: {cfg.description}", file=sys.stderr, flush=True)
 
-    sets = []
-    for k in range(args.sets):
-        v = wl.make_values(batch, device=dev, seed=k, poison_nan=False)
-        sets.append(v)
+    sets = [wl.make_values(batch, device=dev, seed=k, poison_nan=False) for k in range(args.sets)]
     bt = torch.from_numpy(batch.block_tables).to(dev)
     ctx = torch.from_numpy(batch.context_lens).to(dev)
     tseq = torch.from_numpy(batch.token_seq).to(dev)
@@ -418,7 +463,6 @@ def main():
     ws_bytes = pa.pa_decode_workspace_bytes(sets[0]["k_pool"], cfg.num_seqs, cfg.num_q_heads,
                                             cfg.head_dim, batch.max_context_len, part)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
     kv_bytes = batch.kv_bytes()
     n_pairs = batch.copy_pairs.shape[0]
     # tables that share physical blocks (shared prompts) are read through the caches
@@ -452,23 +496,23 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     t_start.record(stream)
     for k in range(args.steps):
         step(k, evs[k])
     t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     ms_step_eager = t_start.elapsed_time(t_end) / args.steps
     cache_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     attn_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
     red_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
     attn_avg = float(np.mean(attn_us))
-    print(f"[bench] {args.steps} eager steps: {ms_step_eager * 1e3:.1f} us/step (wall "
-          f"{wall / args.steps * 1e6:.1f} us); attention {attn_avg:.1f} us (p10 "
-          f"{np.percentile(attn_us, 10):.1f}, p90 {np.percentile(attn_us, 90):.1f}), reduce "
-          f"{np.mean(red_us):.1f} us, cache write {np.mean(cache_us):.1f} us",
-          file=sys.stderr, flush=True)
+    # with one partition per context pa_decode_reduce launches nothing: its events then time only
+    # the gap between two launches, which is not part of pa_decode
+    red_avg = float(np.mean(red_us)) if ws_bytes > 0 else 0.0
+    print(f"[bench] {cfg.name}: {args.steps} eager steps {ms_step_eager * 1e3:.1f} us/step; "
+          f"attention {attn_avg:.1f} us (p10 {np.percentile(attn_us, 10):.1f}, p90 "
+          f"{np.percentile(attn_us, 90):.1f}), reduce {red_avg:.1f} us, cache write "
+          f"{np.mean(cache_us):.1f} us", file=sys.stderr, flush=True)
 
     # pass 2, the timed region: the whole step captured once per input set in a HIP graph (the
     # library allocates nothing and every launch goes to torch's current stream, which is the
@@ -492,50 +536,25 @@ def main():
         g_end.record()
         torch.cuda.synchronize()
         ms_step = g_start.elapsed_time(g_end) / args.steps
-        print(f"[bench] {args.steps} graph-replayed steps: {ms_step * 1e3:.1f} us/step",
-              file=sys.stderr, flush=True)
+        del graphs
+        print(f"[bench] {cfg.name}: {args.steps} graph-replayed steps {ms_step * 1e3:.1f} "
+              "us/step", file=sys.stderr, flush=True)
 
-    if args.copy_calibration:
-        copy_calibration(dev)
-
-    achieved = kv_bytes / (attn_avg * 1e-6) / 1e9
+    unique = batch.unique_kv_bytes()
+    # the bytes the attention must bring from HBM: every context token's K and V, counted once
+    # per distinct (block, slot) when sequences share blocks
+    algo_bytes = unique if shared else kv_bytes
+    achieved = algo_bytes / (attn_avg * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": recorded_traffic(cfg.name),
                 "kernel": "decode_attention_kernel", "avg_us": round(attn_avg, 2),
-                "bytes_per_launch": kv_bytes}
-
-    swap = None
-    if args.swap:
-        swap = swap_rate(cfg, batch, sets[0], stream)
-
-    paging = None
-    if args.paging_overhead:
-        paging = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared, stream)
-
-    budget = 0.0 if args.no_cpu_baseline else 5.0
-    prefill = [prefill_rate(n, args.steps, args.warmup, stream, budget) for n in prefill_names]
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        host = {name: host_storage(sets[0][name]) for name in ("query", "k_pool", "v_pool")}
-        cpu = cpu_baseline(batch, host, args.cpu_budget)
-
-    copy_gbps = copy_bandwidth(dev)
-    value = kv_bytes / (ms_step * 1e-3) / 1e9
-    line = {
-        "metric": "pa_decode KV-read HBM GB/s (fraction of MI355X peak) + decode tokens/s",
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic",
+                "bytes_per_launch": algo_bytes}
+    decode_us = attn_avg + red_avg
+    step_algo_gbps = algo_bytes / (ms_step * 1e-3) / 1e9
+    decode_algo_gbps = algo_bytes / (decode_us * 1e-6) / 1e9
+    res = {
+        "workload": cfg.name, "description": cfg.description, "dtype": cfg.dtype,
         "config": {"workload": cfg.name, "num_seqs": cfg.num_seqs,
                    "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "block_size": cfg.block_size,
@@ -545,24 +564,160 @@ def main():
                    "copy_pairs": int(n_pairs), "shared_blocks": bool(shared),
                    "blocks_distinct": batch.block_counts()[0],
                    "blocks_if_unshared": batch.block_counts()[1]},
-        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "step_us": round(ms_step * 1e3, 2),
+        "step_us_eager": round(ms_step_eager * 1e3, 2),
+        "step_gbps": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_algo_gbps / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(cfg.num_seqs / (ms_step * 1e-3), 1),
-        "tokens_per_s_attention_only": round(
-            cfg.num_seqs / ((attn_avg + float(np.mean(red_us))) * 1e-6), 1),
+        "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),
+                      "attention": round(attn_avg, 2), "partition_reduce": round(red_avg, 2),
+                      "pa_decode": round(decode_us, 2)},
+        "pa_decode_gbps": round(kv_bytes / (decode_us * 1e-6) / 1e9, 1),
+        "pa_decode_frac_of_peak": round(decode_algo_gbps / HBM_PEAK_GBPS, 4),
+        # GB/s fields count every context token's K and V (the metric's KV-read bytes); the
+        # fractions of peak count the bytes that must come from HBM (distinct blocks when
+        # sequences share them)
+        "frac_basis": "unique_kv_bytes" if shared else "kv_bytes",
+        "tokens_per_s_attention_only": round(cfg.num_seqs / (decode_us * 1e-6), 1),
+        "roofline": roofline,
+    }
+    if shared:
+        res["logical_kv_bytes"] = kv_bytes
+        res["unique_kv_bytes"] = unique
+        res["attention_logical_gbps"] = round(kv_bytes / (attn_avg * 1e-6) / 1e9, 1)
+    if swap:
+        res["swap"] = swap_rate(cfg, batch, sets[0], stream)
+    if paging:
+        res["paging_overhead"] = paging_overhead(args, cfg, batch, sets, outs, ws, part, shared,
+                                                 stream)
+    if cpu:
+        host = {n: host_storage(sets[0][n]) for n in ("query", "k_pool", "v_pool")}
+        del sets, outs, ws
+        torch.cuda.empty_cache()
+        one = cpu_baseline(batch, host, args.cpu_budget)
+        allc = cpu_baseline_all_cores(batch, host, host_workers())
+        allc["one_core"] = one
+        res["cpu_baseline"] = allc
+        print(f"[bench] {cfg.name}: oracle {allc['value']} GB/s on {allc['cores']} cores, "
+              f"{one['value']} GB/s on one", file=sys.stderr, flush=True)
+        del host
+    else:
+        res["cpu_baseline"] = None
+        del sets, outs, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="opt13b_fp16", help="the headline decode workload")
+    ap.add_argument("--also", default="gqa_bf16,long_bf16,cow_fp16,tiny_fp32",
+                    help="comma-separated decode workloads measured in the same run and reported "
+                         "under 'workloads' (empty for none)")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition size in tokens for the headline workload; -1 = the "
+                         "workload's own setting")
+    ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="run the headline workload at this block size (8, 16 or 32) instead of "
+                         "its own; the pool is then sized for the blocks in use (1.25x)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of the one-thread oracle sample per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager launches only (no HIP-graph replay of the step)")
+    ap.add_argument("--paging-overhead", action="store_true",
+                    help="also time pa_decode against its contiguous twin (no block table) on a "
+                         "contiguously laid out copy of the headline batch")
+    ap.add_argument("--swap", action="store_true",
+                    help="also time swapping every block of half the sequences out to pinned "
+                         "host memory and back (pa_swap_blocks)")
+    ap.add_argument("--prefill", default="prefill_bf16",
+                    help="comma-separated prefill workloads to time as well (pa_prefill), e.g. "
+                         "prefill_bf16,chunked_fp16; empty for none")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the --prefill workloads and print their JSON (--block-size "
+                         "and --placement then apply to them)")
+    ap.add_argument("--placement", default="", choices=["", "shuffled", "contiguous"],
+                    help="with --prefill-only: physical block placement of the prefill batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    prefill_names = [n for n in args.prefill.split(",") if n]
+    if args.prefill_only:
+        budget = 0.0 if args.no_cpu_baseline else 5.0
+        over = {}
+        if args.block_size:
+            over.update(block_size=args.block_size, num_blocks=0)
+        if args.placement:
+            over.update(placement=args.placement)
+        res = [prefill_rate(n, args.steps, args.warmup, stream, budget, **over)
+               for n in prefill_names]
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"prefill": res}), flush=True)
+        return
+
+    cpu = not args.no_cpu_baseline
+    head = decode_rate(args.config, args, dev, stream, part_override=args.partition,
+                       block_size=args.block_size, cpu=cpu, paging=args.paging_overhead,
+                       swap=args.swap)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    others = [decode_rate(n, args, dev, stream, cpu=cpu)
+              for n in args.also.split(",") if n and n != args.config]
+    prefill = [prefill_rate(n, args.steps, args.warmup, stream, 5.0 if cpu else 0.0)
+               for n in prefill_names]
+    copy_gbps = copy_bandwidth(dev)
+
+    value = head["step_gbps"]
+    line = {
+        "metric": "pa_decode KV-read HBM GB/s (fraction of MI355X peak) + decode tokens/s",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_us"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "frac_of_peak": head["step_frac_of_peak"],
+        "tokens_per_s": head["tokens_per_s"],
+        "tokens_per_s_attention_only": head["tokens_per_s_attention_only"],
+        "pa_decode_gbps": head["pa_decode_gbps"],
+        "pa_decode_frac_of_peak": head["pa_decode_frac_of_peak"],
         "hbm_copy_gbps": copy_gbps,
         "frac_of_copy": round(value / copy_gbps, 4),
         "launch": "eager" if args.eager else "hip_graph",
-        "ms_per_step_eager": round(ms_step_eager, 5),
-        "kernel_us": {"cache_write_and_copies": round(float(np.mean(cache_us)), 2),
-                      "attention": round(attn_avg, 2),
-                      "partition_reduce": round(float(np.mean(red_us)), 2)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
+        "ms_per_step_eager": round(head["step_us_eager"] / 1e3, 5),
+        "kernel_us": head["kernel_us"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    if paging is not None:
-        line["paging_overhead"] = paging
-    if swap is not None:
-        line["swap"] = swap
+    for key in ("paging_overhead", "swap"):
+        if key in head:
+            line[key] = head[key]
+    if others:
+        line["workloads"] = others
     if prefill:
         line["prefill"] = prefill
     print(json.dumps(line), flush=True)

@@ -361,6 +361,20 @@ class DecodeBatch:
         c = self.cfg
         return int(self.context_lens.astype(np.int64).sum()) * c.num_kv_heads * c.head_dim * 2 * c.esz
 
+    def unique_kv_bytes(self) -> int:
+        """K plus V bytes of the distinct (physical block, slot) pairs the attention reads: what
+        must come from HBM at least once when sequences share blocks (equal to kv_bytes when
+        none are shared)."""
+        c = self.cfg
+        B = c.block_size
+        used = {}
+        for s in range(c.num_seqs):
+            n = int(self.context_lens[s])
+            for j in range(-(-n // B)):
+                b = int(self.block_tables[s, j])
+                used[b] = max(used.get(b, 0), min(B, n - j * B))
+        return sum(used.values()) * c.num_kv_heads * c.head_dim * 2 * c.esz
+
 
 def _draw_context_lens(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
     kind = cfg.ctx[0]
