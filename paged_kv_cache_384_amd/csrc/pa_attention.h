@@ -128,6 +128,7 @@ struct BlockStep {
                                              std::make_integer_sequence<int, kLoads>{});
     }
 
+    // one value row at a time: widen, products, then the refill of that row's registers
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       float v[kEpp];
@@ -142,10 +143,7 @@ struct BlockStep {
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(pw[hh][i], v[e], acc[hh][e]);
-    }
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
+      if constexpr (kPrefetch) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
     }
   }
 };
@@ -220,16 +218,15 @@ struct MfmaBlockStep {
 #pragma unroll
         for (int e = 0; e < kEpp; ++e) acc[hh][e] *= ch[hh];
     }
-    float pw[4][NH];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pi = exp2_fast(sc[i] - m);
-      lsum += pi;
-      bcast_heads(pi, pw[i], std::make_integer_sequence<int, NH>{});
-    }
-
+    // value row i of this lane (token 4(l/16) + i) at a time: its weight for each head, the
+    // widened row, the products, then the refill of that row's registers, so that only one
+    // row's temporaries are live at once
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+      const float pi = exp2_fast(sc[i] - m);
+      lsum += pi;
+      float w[NH];
+      bcast_heads(pi, w, std::make_integer_sequence<int, NH>{});
       float v[kEpp];
       Widen<dt>::run(vb[i], v);
       if constexpr (!kPrefetch) {
@@ -241,11 +238,8 @@ struct MfmaBlockStep {
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(pw[i][hh], v[e], acc[hh][e]);
-    }
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
+        for (int e = 0; e < kEpp; ++e) acc[hh][e] = __builtin_fmaf(w[hh], v[e], acc[hh][e]);
+      if constexpr (kPrefetch) vb[i] = load16_kv<kStream>(next.v + i * G::kRowBytes);
     }
   }
 };
@@ -296,20 +290,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
 
   // ---- this wavefront's groups -------------------------------------------------------------
   // a contiguous range [jb, je) of the partition's groups. Paged: the physical ids of their
-  // blocks are wave-uniform and come straight from the table with scalar loads ([anal] §3: the
-  // kernel looks each logical block up in the block table), clamped into [0, NB). The
-  // contiguous twin has no table: block j of sequence s is physical block s * max_blocks + j.
+  // blocks are looked up in the table ([anal] §3: the kernel looks each logical block up in the
+  // block table) once, up front, one block per lane (a wavefront covers at most 64 blocks: 32
+  // groups of a 2048-token partition, two 8-token blocks each), clamped into [0, NB); each step
+  // then takes its id from that register with readlane, so no table read stands between
+  // consuming one block and requesting the next. The contiguous twin has no table: block j of
+  // sequence s is physical block s * max_blocks + j.
   const int64_t row0 = static_cast<int64_t>(s) * a.max_blocks + start / B;
-  [[maybe_unused]] const int32_t* bt_row = a.block_tables + row0;
   const int per_wave = ngroups / kWaves;
   const int extra = ngroups % kWaves;
   const int jb = wave * per_wave + min(wave, extra);
   const int je = jb + per_wave + (wave < extra ? 1 : 0);
   const int num_blocks = a.num_blocks;
+  const int wb0 = jb * kGroupTokens / B;  // the wavefront's first block (of the partition)
+  [[maybe_unused]] int wave_ids = 0;
+  if constexpr (kPaged) {
+    const int jj = wb0 + lane;
+    if (jj < nblocks) {
+      const int id = a.block_tables[row0 + jj];
+      wave_ids = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+    }
+  }
   auto block_id = [&](int j) -> int {
     if constexpr (kPaged) {
-      const int id = bt_row[j];
-      return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+      return __builtin_amdgcn_readlane(wave_ids, j - wb0);
     } else {
       const int64_t id = row0 + j;
       return id >= num_blocks ? num_blocks - 1 : static_cast<int>(id);
@@ -393,14 +397,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   u32x4 kA[kLoads], vA[kLoads];
   [[maybe_unused]] u32x4 kB[kLoads], vB[kLoads];
   auto load_block = [&](int jj, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads]) {
-    const GroupPtrs p = group_ptrs(jj < je ? jj : ngroups - 1);
+    // past the wavefront's range: its own last group again (loaded, never used)
+    const GroupPtrs p = group_ptrs(jj < je ? jj : je - 1);
 #pragma unroll
     for (int c = 0; c < kLoads; ++c) kr[c] = load16_kv<kStream>(p.k + c * G::kChunkRowBytes);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) vr[i] = load16_kv<kStream>(p.v + i * G::kRowBytes);
   };
-  load_block(jb, kA, vA);
-  if constexpr (kDepth == 2) load_block(jb + 1, kB, vB);
+  if (jb < je) {  // a wavefront without groups (partitions of fewer than 4) loads nothing
+    load_block(jb, kA, vA);
+    if constexpr (kDepth == 2) load_block(jb + 1, kB, vB);
+  }
 
   // drives one step type over the wavefront's blocks [jb, je)
   auto stream_blocks = [&](auto& full, auto& tail, auto&... state) {
