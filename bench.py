@@ -435,6 +435,42 @@ def prefill_rate(name, steps, warmup, stream, cpu_budget=0.0, **overrides):
             "cpu_baseline": cpu}
 
 
+def tile_read_reference(sets, nbytes, tile_bytes, steps, stream):
+    """pa_measure_tile_read over as many K+V bytes as ``nbytes``: whole tiles of the workload's
+    own pools in a seeded random order, rotating over the input sets like the decode steps, HIP
+    events on the stream. What plain reads of the decode access pattern reach at this size."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_384_amd as pa
+    pool = sets[0]["k_pool"]
+    total = pool.numel() * pool.element_size() // tile_bytes
+    n = min(total, max(1, round(nbytes / (2 * tile_bytes))))
+    order = np.random.default_rng(1234).permutation(total)[:n].astype(np.int32)
+    tiles = torch.from_numpy(order).to(pool.device)
+    sink = torch.empty((n + 31) // 32, dtype=torch.int32, device=pool.device)
+
+    def once(k):
+        v = sets[k % len(sets)]
+        pa.pa_measure_tile_read(v["k_pool"], v["v_pool"], tiles, tile_bytes, sink)
+
+    for k in range(3):
+        once(k)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        once(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    read = 2 * n * tile_bytes
+    gbps = read / (us * 1e-6) / 1e9
+    return {"tiles": n, "tile_bytes": tile_bytes, "bytes": read, "us": round(us, 2),
+            "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=True,
                 paging=False, swap=False):
     """One decode workload: K eager steps with HIP events around every kernel, then K
@@ -550,6 +586,15 @@ def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=
                 "traffic": recorded_traffic(cfg.name),
                 "kernel": "decode_attention_kernel", "avg_us": round(attn_avg, 2),
                 "bytes_per_launch": algo_bytes}
+    ref = None
+    if kv_bytes >= (64 << 20):  # a latency case below that
+        tile_bytes = cfg.block_size * cfg.head_dim * cfg.esz
+        ref = tile_read_reference(sets, algo_bytes, tile_bytes, args.steps, stream)
+        roofline["reference_gbps"] = ref["gbps"]
+        roofline["frac_of_reference"] = round(achieved / ref["gbps"], 4)
+        print(f"[bench] {cfg.name}: random-tile read of {ref['bytes'] / 1e9:.3f} GB: "
+              f"{ref['us']:.1f} us = {ref['gbps']:.0f} GB/s; attention at "
+              f"{roofline['frac_of_reference']:.3f} of it", file=sys.stderr, flush=True)
     decode_us = attn_avg + red_avg
     step_algo_gbps = algo_bytes / (ms_step * 1e-3) / 1e9
     decode_algo_gbps = algo_bytes / (decode_us * 1e-6) / 1e9
@@ -580,6 +625,7 @@ def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=
         "frac_basis": "unique_kv_bytes" if shared else "kv_bytes",
         "tokens_per_s_attention_only": round(cfg.num_seqs / (decode_us * 1e-6), 1),
         "roofline": roofline,
+        "tile_read_reference": ref,
     }
     if shared:
         res["logical_kv_bytes"] = kv_bytes

@@ -63,7 +63,7 @@ extern "C" {
 #define PA_API
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 #define PA_MAX_PARTITION_TOKENS 2048 /* largest partition_size pa_decode accepts */
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -390,6 +390,28 @@ PA_API pa_status pa_validate_writes(const pa_cache_desc* c, const int32_t* block
                                     const int32_t* token_seq, const int32_t* token_pos,
                                     int32_t num_tokens, const int32_t* src_dst, int32_t num_pairs,
                                     int32_t* violations, void* stream);
+
+/*
+ * pa_measure_tile_read — measurement only: the bandwidth reference of the decode access pattern.
+ * ([anal] §2 and §5: blocks sit wherever the pool had room, and decode attention is bound by
+ *  reading them.)
+ *
+ * Reads tiles tiles[0..num_tiles) — tile t is bytes [t * tile_bytes, (t + 1) * tile_bytes) — of
+ * both pool_a and pool_b, with the attention kernel's loads (non-temporal 16-byte wave loads,
+ * 1 KiB contiguous per instruction), kMeasureTilesPerWave = 32 consecutive entries of `tiles`
+ * per wavefront, and writes to sink[w] the XOR of every 32-bit word wavefront w read (so the
+ * reads cannot be dropped, and a test can check them). Timing it over as many bytes as a decode
+ * step reads, in a random tile order, gives what plain reads of that pattern and size reach.
+ *   pool_a, pool_b  device, at least (max tile index + 1) * tile_bytes bytes each
+ *   tiles           device int32 [num_tiles], tile indices (not checked against the pools)
+ *   tile_bytes      a multiple of 1024, at most 65536
+ *   sink            device uint32 [ceil(num_tiles / 32)]
+ * Errors: checked on the host before the launch (PA_ERR_NULL / SHAPE / ALIGN); a failed launch
+ * gives PA_ERR_LAUNCH. num_tiles = 0 returns PA_OK.
+ */
+PA_API pa_status pa_measure_tile_read(const void* pool_a, const void* pool_b,
+                                      const int32_t* tiles, int32_t num_tiles,
+                                      int32_t tile_bytes, uint32_t* sink, void* stream);
 
 /* Static description of a status code (never NULL; "unknown status" for a value that is not a
  * pa_status). The code is taken as a plain int so that any value a caller passes is defined. */

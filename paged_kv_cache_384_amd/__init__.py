@@ -28,11 +28,12 @@ __all__ = [
     "pa_decode_attention", "STATIC_WORKSPACE_BYTES",
     "pa_decode_reduce", "pa_decode_contiguous", "pa_prefill", "pa_swap_blocks",
     "pa_decode_workspace_bytes", "pa_copy_blocks", "pa_validate_tables", "pa_validate_writes",
+    "pa_measure_tile_read",
     "pa_status_string",
     "pa_abi_version", "ABI_VERSION", "CACHE_SHARED_BLOCKS", "DTYPE_CODES", "EXPORTED_SYMBOLS",
 ]
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 STATIC_WORKSPACE_BYTES = 32 * 1024 * 1024  # PA_STATIC_WORKSPACE_BYTES
 CACHE_SHARED_BLOCKS = 1  # pa_cache_desc.flags bit: blocks may be shared by several sequences
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
@@ -44,7 +45,8 @@ EXPORTED_SYMBOLS = ["pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_dec
                     "pa_decode_static",
                     "pa_decode_attention", "pa_decode_reduce", "pa_decode_contiguous",
                     "pa_prefill", "pa_copy_blocks", "pa_swap_blocks", "pa_validate_tables",
-                    "pa_validate_writes", "pa_status_string", "pa_abi_version"]
+                    "pa_validate_writes", "pa_measure_tile_read", "pa_status_string",
+                    "pa_abi_version"]
 
 
 class CacheDesc(ctypes.Structure):
@@ -101,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.pa_validate_writes.argtypes = [_desc_p, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _i32, _vp,
                                          _vp]
         L.pa_validate_writes.restype = ctypes.c_int
+        L.pa_measure_tile_read.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp]
+        L.pa_measure_tile_read.restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
@@ -444,3 +448,19 @@ def pa_swap_blocks(dst_key, dst_value, src_key, src_value, src_dst, *, head_dim:
             ctypes.byref(sd), ptr(src_key, "src_key"), ptr(src_value, "src_value"),
             _vp(src_dst.data_ptr()), src_dst.numel() // 2, _stream(gpu, stream))
     _check(lib().pa_swap_blocks(*args), "pa_swap_blocks")
+
+
+def pa_measure_tile_read(pool_a, pool_b, tiles, tile_bytes: int, sink=None, *, stream=None):
+    """Measurement only: read tiles ``tiles`` (int32, GPU) of ``tile_bytes`` from both GPU
+    tensors with the attention kernel's loads; returns ``sink`` (uint32 per 32 tiles, the XOR of
+    the words each wavefront read; allocated if None)."""
+    import torch
+    n = tiles.numel()
+    if sink is None:
+        sink = torch.empty((n + 31) // 32, dtype=torch.int32, device=tiles.device)
+    if sink.numel() < (n + 31) // 32:
+        raise ValueError("sink must hold one word per 32 tiles")
+    args = (_dev(pool_a, "pool_a"), _dev(pool_b, "pool_b"), _dev(tiles, "tiles", torch.int32),
+            n, int(tile_bytes), _dev(sink, "sink"), _stream(tiles, stream))
+    _check(lib().pa_measure_tile_read(*args), "pa_measure_tile_read")
+    return sink

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_api.cpp", "pa_cache.hip", "pa_attention_b8.hip", "pa_attention_b16.hip",
-           "pa_attention_b32.hip", "pa_reduce.hip", "pa_prefill.hip"]
+           "pa_attention_b32.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_measure.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32 (plain fp32 VALU only).
 # The host pass warns that it does not know the feature; that is expected.

@@ -517,6 +517,30 @@ pa_status pa_swap_blocks(const pa_cache_desc* dst, void* dst_key, void* dst_valu
   return PA_OK;
 }
 
+pa_status pa_measure_tile_read(const void* pool_a, const void* pool_b, const int32_t* tiles,
+                               int32_t num_tiles, int32_t tile_bytes, uint32_t* sink,
+                               void* stream) {
+  if (num_tiles < 0 || tile_bytes <= 0 || tile_bytes % 1024 != 0 || tile_bytes > 65536)
+    return PA_ERR_SHAPE;
+  if (num_tiles == 0) return PA_OK;
+  if (!pool_a || !pool_b || !tiles || !sink) return PA_ERR_NULL;
+  if (!aligned(pool_a, 16) || !aligned(pool_b, 16) || !aligned(tiles, 4) || !aligned(sink, 4))
+    return PA_ERR_ALIGN;
+  const int64_t waves = (static_cast<int64_t>(num_tiles) + pa::kMeasureTilesPerWave - 1) /
+                        pa::kMeasureTilesPerWave;
+  if ((waves + 3) / 4 > kMaxWorkgroups) return PA_ERR_SHAPE;
+  pa::MeasureArgs a;
+  a.pool_a = static_cast<const uint8_t*>(pool_a);
+  a.pool_b = static_cast<const uint8_t*>(pool_b);
+  a.tiles = tiles;
+  a.sink = sink;
+  a.num_tiles = num_tiles;
+  a.tile_bytes = tile_bytes;
+  if (pa::launch_tile_read(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";

@@ -72,6 +72,17 @@ struct ValidateWritesArgs {
   int32_t block_size;
 };
 
+// pa_measure_tile_read: tiles of two pools read in a given order.
+constexpr int kMeasureTilesPerWave = 32;
+struct MeasureArgs {
+  const uint8_t* pool_a;
+  const uint8_t* pool_b;
+  const int32_t* tiles;  // [num_tiles] tile indices into both pools
+  uint32_t* sink;        // [ceil(num_tiles / kMeasureTilesPerWave)] XOR of the words read
+  int64_t num_tiles;
+  int32_t tile_bytes;
+};
+
 // One launch of the attention stage covers every (KV head, sequence, head group, partition).
 struct DecodeArgs {
   const uint8_t* k_pool;
@@ -138,6 +149,7 @@ hipError_t launch_reshape_and_cache(DType dt, int head_dim, int block_size,
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 hipError_t launch_validate_writes(const ValidateWritesArgs& a, hipStream_t stream);
+hipError_t launch_tile_read(const MeasureArgs& a, hipStream_t stream);
 hipError_t launch_decode_attention_b8(DType dt, int head_dim, const DecodeArgs& a,
                                       hipStream_t stream);
 hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs& a,

@@ -402,3 +402,19 @@ def test_validate_writes_validation(L):
     # nothing to compare: only the count's pointer is needed (a launch follows, so stop it there)
     none = {k: P(0) for k in ("bt", "seq", "pos", "pairs", "out")}
     assert vw(T=0, npairs=0, S=0, maxb=0, ptrs=none) == NULL
+
+
+def test_measure_tile_read_validation(L):
+    """Sizes, pointers and alignment checked before the launch."""
+    def mt(n=64, tb=4096, ptrs=None):
+        p = ptrs or {}
+        return L.pa_measure_tile_read(p.get("a", GOOD), p.get("b", GOOD), p.get("t", GOOD), n,
+                                      tb, p.get("s", GOOD), P(0))
+    assert mt(n=-1) == SHAPE
+    for tb in (0, 1000, 1536, 65536 + 1024):
+        assert mt(tb=tb) == SHAPE, tb
+    for k in ("a", "b", "t", "s"):
+        assert mt(ptrs={k: P(0)}) == NULL, k
+    assert mt(ptrs={"a": ODD}) == ALIGN
+    assert mt(ptrs={"t": P(0x10002)}) == ALIGN
+    assert mt(n=0, ptrs={k: P(0) for k in "abts"}) == OK
