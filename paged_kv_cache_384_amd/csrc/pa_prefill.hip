@@ -14,11 +14,11 @@
 // Workgroup: 256 threads (four wavefronts) own 128 consecutive queries of one (sequence, query
 // head); each wavefront owns 32 of them as two 16-query MFMA columns. The workgroup walks the
 // sequence's tokens in tiles of 64, from token 0 to the last position its queries can see:
-//   * the tile's key rows and value rows are gathered through the block table into LDS (double
-//     buffered, the next tile's global loads in flight while the current one is computed), one
-//     row per token for each, the head vector plus 32 bytes: 288 bytes at head_dim 128 (72
-//     dwords, 8 more than a multiple of the 64 banks: the operand reads below are free of bank
-//     conflicts at that stride on gfx950, measured), 160 bytes at head_dim 64 (40 dwords);
+//   * the tile's keys and values are gathered through the block table straight into LDS by
+//     global_load_lds_dwordx4 (no trip through registers; double buffered, the next tile's loads
+//     in flight while the current one is computed). Keys land in the order the matrix-core
+//     operand reads want them; values in token rows whose 16-byte pieces are rotated by the
+//     token, so the transposing reads below meet every bank once;
 //   * each wavefront forms S^T = K Q^T: A = 16 tokens x 32 dims read from LDS, B = its queries
 //     held in registers since the start. Lane l gets query l%16 and tokens 4(l/16)..4(l/16)+3 of
 //     each 16-token block;
@@ -65,6 +65,13 @@ __device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// global_load_lds_dwordx4: 16 bytes from global address g straight into LDS, lane i's bytes
+// landing at lds + 16 * i (the LDS base is taken from the first lane); counted by vmcnt.
+__device__ __forceinline__ void load_lds16(const uint8_t* g, uint8_t* lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds), 16, 0, 0);
+}
+
 // Maximum over lanes l, l^16, l^32, l^48 (the four rows of 16 lanes), in every lane: a
 // v_permlane16_swap and a v_permlane32_swap of the value with itself give each lane its partner
 // in the other half of the row pair / wave half.
@@ -94,7 +101,7 @@ template <> struct Pack2<DType::BF16> {
 }  // namespace
 
 // Workgroups per CU: two at head_dim 128 (eight wavefronts, two per SIMD, registers capped at
-// 256 per lane, 72 KiB of LDS each), three at head_dim 64 (registers capped at 168, 40 KiB of
+// 256 per lane, 64 KiB of LDS each), three at head_dim 64 (registers capped at 168, 32 KiB of
 // LDS each), so one wavefront's softmax overlaps another's matrix-core work.
 template <int D> constexpr int prefill_waves_per_simd() { return D == 64 ? 3 : 2; }
 
@@ -106,11 +113,21 @@ void prefill_kernel(PrefillArgs a) {
   static_assert(G::kEsz == 2, "matrix-core prefill takes 16-bit elements");
   constexpr int kChunks = D / 32;          // 64-byte chunks (32 dims) per key row
   constexpr int kDBlocks = D / 16;         // 16-dim output blocks
-  constexpr int kRow = D * 2 + 32;         // LDS row of one token (keys or values), padded
-  constexpr int kVPieces = D / 32;         // 16-byte value pieces per lane per tile
-  static_assert(D * 2 <= kRow, "a token's head vector fits one LDS row");
-  __shared__ __align__(16) uint8_t k_s[2][kTileT * kRow];
-  __shared__ __align__(16) uint8_t v_s[2][kTileT * kRow];
+  constexpr int kVRow = D * 2;             // LDS value row of one token (unpadded)
+  constexpr int kPPR = kVRow / 16;         // 16-byte pieces per value row
+  constexpr int kRPI = 1024 / kVRow;       // value rows one wave load fills
+  constexpr int kVLoads = 16 / kRPI;       // wave loads per wavefront per tile (its 16 tokens)
+  constexpr int kKLoads = kChunks;         // key wave loads per wavefront per tile
+  constexpr int kTileBytesLds = kTileT * D * 2;  // one tile of keys (or of values) in LDS
+  static_assert(kRPI * kVLoads == 16 && kRPI <= B, "a value wave load stays inside one block");
+  // two buffers of each, as separate arrays: every access below names its buffer at compile time
+  // (the step loop is unrolled by two), so the compiler can tell that a tile's operand reads and
+  // the next tile's loads into the other buffer never overlap, and does not make the reads wait
+  // for those loads
+  __shared__ __align__(1024) uint8_t k_s0[kTileBytesLds];
+  __shared__ __align__(1024) uint8_t k_s1[kTileBytesLds];
+  __shared__ __align__(1024) uint8_t v_s0[kTileBytesLds];
+  __shared__ __align__(1024) uint8_t v_s1[kTileBytesLds];
 
   // ---- which queries ---------------------------------------------------------------------
   // Workgroups come in units whose members read the same key/value tiles and run as
@@ -157,7 +174,7 @@ void prefill_kernel(PrefillArgs a) {
   const int n_steps = p_last < 0 ? 0 : p_last / kTileT + 1;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;  // MFMA column (query) / row (token, dim) within a 16-block
   const int grp = lane >> 4;  // MFMA lane group: k values 8*grp .. 8*grp+7
@@ -178,47 +195,76 @@ void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < kChunks; ++c) qf[qb][c] = load16(row + c * 64);
   }
 
-  // ---- gathering a tile: the loads each thread issues --------------------------------------
-  // Lane (col, grp) of wavefront w loads token 16w + col of the tile: of its key, 16-byte piece
-  // grp of each 64-byte chunk (a wave load covers 16 tokens' chunk c: one contiguous 1 KiB key
-  // chunk row at B = 16); of its value, pieces grp + 4i (a wave load covers 64 bytes of each
-  // of 16 token rows).
-  const int ktok = wave * 16 + col;
+  // ---- gathering a tile: wave loads straight into LDS ------------------------------------
+  // Each lane's 16 bytes of a wave load land at (wave-uniform LDS base) + 16 * lane, so the LDS
+  // layout is chosen by which global bytes each lane requests:
+  //   keys, in matrix-operand order: the 1 KiB at (tb * kChunks + c) KiB holds, at 16 * lane,
+  //     the A operand lane (col, grp) reads for token block tb and chunk c: token 16 tb + col,
+  //     bytes [64 c + 16 grp, +16) of its key row. Wavefront w loads token block w;
+  //   values, in token rows of kVRow bytes whose 16-byte pieces are rotated by the token: piece p
+  //     of token t sits at piece slot p ^ vswz(t), so that the transposing operand reads below
+  //     (each half-wavefront: 8 tokens, 2 adjacent pieces each) meet all 64 banks once.
+  //     Wavefront w loads rows 16 w .. 16 w + 15, kRPI rows per wave load.
+  // A wavefront's 16 tokens lie in one block (B >= 16) or two (B = 8; lanes col >= 8, and value
+  // loads of rows 8..15, take the second), so each load is a block address plus a per-lane offset
+  // that is the same for every tile.
+  auto vswz = [](int t) -> int {  // piece rotation of value row t (even, below kPPR)
+    return 2 * ((t / (256 / kVRow)) & (kPPR / 2 - 1));
+  };
+  const int ktok = wave * 16 + col;  // this lane's key token of the tile
   const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
-  // the table entry of token t (clamped to the context, so entries past it are never read), and
-  // the byte offset of (block b, this KV head) with b clamped into the pool
+  // the table entry of the block holding token t (t clamped to the context, so entries past it
+  // are never read); one per lane: this lane's key token, 2 tiles ahead of its use
   auto table_block = [&](int t) -> int {
     t = t < ctx ? t : ctx - 1;
     return a.block_tables[table_row + t / B];
   };
+  // byte offset of (block b clamped into the pool, this KV head)
   auto tile_of = [&](int b) -> int64_t {
     b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
     return (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * G::kTileBytes;
   };
-  u32x4 kr[kChunks];
-  u32x4 vr[kVPieces];
-  auto load_tile = [&](int64_t tile) {
-    const uint8_t* kp = a.k_pool + tile + (ktok % B) * 64 + grp * 16;
+  // per-lane offsets inside a block, the same for every tile (T0 is a multiple of 64 >= B)
+  const int kl_off = (ktok % B) * 64 + grp * 16;
+  int vl_off[kVLoads];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) kr[c] = load16(kp + c * G::kChunkRowBytes);
-    const uint8_t* vp = a.v_pool + tile + (ktok % B) * G::kRowBytes + grp * 16;
-#pragma unroll
-    for (int i = 0; i < kVPieces; ++i) vr[i] = load16(vp + i * 64);
-  };
-  auto store_tile = [&](int buf, int T0) {
-    if (T0 + kTileT > ctx && T0 + ktok >= ctx) {  // past the context's end: zeros
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) kr[c] = zero;
-#pragma unroll
-      for (int i = 0; i < kVPieces; ++i) vr[i] = zero;
+  for (int i = 0; i < kVLoads; ++i) {
+    const int r = wave * 16 + i * kRPI + lane / kPPR;  // value row (token) this lane fills
+    vl_off[i] = (r % B) * kVRow + ((lane % kPPR) ^ vswz(r)) * 16;
+  }
+  // kid: this lane's table entry for its key token of the tile. The value rows of a wave load
+  // all lie in the block of the wavefront's tokens 0-7 (lanes col < 8) or 8-15 (col >= 8).
+  auto load_tile = [&](uint8_t* kdst, uint8_t* vdst, int kid) {
+    const int64_t kblk = tile_of(kid);
+    [[maybe_unused]] int64_t lo = kblk, hi = kblk;
+    if constexpr (B < 16) {
+      lo = tile_of(__shfl(kid, 0, 64));
+      hi = tile_of(__shfl(kid, 8, 64));
     }
-    uint8_t* kd = k_s[buf] + ktok * kRow + grp * 16;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) store16(kd + c * 64, kr[c]);
-    uint8_t* vd = v_s[buf] + ktok * kRow + grp * 16;
+    for (int c = 0; c < kKLoads; ++c)
+      load_lds16(a.k_pool + kblk + kl_off + c * G::kChunkRowBytes,
+                 kdst + (wave * kChunks + c) * 1024);
 #pragma unroll
-    for (int i = 0; i < kVPieces; ++i) store16(vd + i * 64, vr[i]);
+    for (int i = 0; i < kVLoads; ++i) {
+      const int64_t vblk = B >= 16 ? kblk : (i * kRPI >= 8 ? hi : lo);
+      load_lds16(a.v_pool + vblk + vl_off[i], vdst + (wave * 16 + i * kRPI) * kVRow);
+    }
+  };
+  // after the wave's loads of tile T0 have landed: zeros over tokens at or past the context's
+  // end (only the context's last tile has any), so whatever the slots past it hold never enters
+  auto zero_tail = [&](uint8_t* kdst, uint8_t* vdst, int T0) {
+    if (T0 + kTileT <= ctx) return;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (T0 + ktok >= ctx) {
+#pragma unroll
+      for (int c = 0; c < kKLoads; ++c)
+        store16(kdst + (wave * kChunks + c) * 1024 + lane * 16, zero);
+    }
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i)
+      if (T0 + wave * 16 + i * kRPI + lane / kPPR >= ctx)
+        store16(vdst + (wave * 16 + i * kRPI) * kVRow + lane * 16, zero);
   };
 
   // ---- running softmax state and output (O^T blocks: dims 16*db + 4*grp + i, query col) ---
@@ -235,16 +281,22 @@ void prefill_kernel(PrefillArgs a) {
   const uint32_t one2 = Pack2<dt>::run(1.0f, 1.0f);
   const u32x4 ones = {one2, one2, one2, one2};
   const float thresh = kRescaleSlackPf;
+  // this lane's transposing-read offsets in a value tile, per 16-dim block db: token
+  // 4grp + col/4 (adding 16 or 32 tokens keeps the piece rotation), piece 2db + (col%4)/2 rotated,
+  // then the lane's 8-byte half
+  // (rotation: piece slot = piece ^ vr_swz, so slot 16-byte offsets are (2db*16) ^ vr_x)
+  const int vr_t = 4 * grp + (col >> 2);
+  const int vr_base = vr_t * kVRow + (col & 1) * 8;
+  const int vr_x = (((col & 3) >> 1) ^ vswz(vr_t)) * 16;
 
   // One key/value tile. Scores stay raw (unscaled) until the exponent, where one fma applies the
   // scale and subtracts the running maximum; the maximum of scaled scores is the scale times the
   // raw maximum because the scale is positive. kMasked: the tile reaches past some column's
   // position, so tokens after it get -inf.
-  auto compute = [&](int buf, int T0, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
+  auto compute = [&](const uint8_t* ktile, const uint8_t* vtile, int T0, bool masked) {
     // S^T blocks: st[qb][tb][i] = score of query 16qb+col, token T0 + 16tb + 4grp + i
     f32x4 st[2][4];
-    const uint8_t* kb = k_s[buf] + col * kRow + grp * 16;
+    const uint8_t* kb = ktile + lane * 16;
     // matrix-core sections run at raised wave priority, so a wavefront that has its operands
     // keeps the matrix pipe fed while the SIMD's other wavefront does its softmax arithmetic
     __builtin_amdgcn_s_setprio(1);
@@ -254,7 +306,7 @@ void prefill_kernel(PrefillArgs a) {
       st[1][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
-        const u32x4 kf = load16(kb + tb * 16 * kRow + c * 64);
+        const u32x4 kf = load16(kb + (tb * kChunks + c) * 1024);
         st[0][tb] = Mfma16x16x32<dt>::run(kf, qf[0][c], st[0][tb]);
         st[1][tb] = Mfma16x16x32<dt>::run(kf, qf[1][c], st[1][tb]);
       }
@@ -263,7 +315,7 @@ void prefill_kernel(PrefillArgs a) {
     float mx[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (kMasked) {
+      if (masked) {
         const int lim = base_p + wj0 + qb * 16 + col - T0 - grp * 4;  // last visible offset
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -310,9 +362,10 @@ void prefill_kernel(PrefillArgs a) {
         pb[qb][ks].w = Pack2<dt>::run(pr[2 * ks + 1][2], pr[2 * ks + 1][3]);
       }
     }
-    // transposing reads: this lane addresses token 4grp + col/4 (+16) of the step, dims
-    // 16db + 4(col%4) .. +3, and receives dim 16db + col of tokens 4grp .. 4grp+3 (16+...)
-    const uint8_t* vb = v_s[buf] + (4 * grp + (col >> 2)) * kRow + 8 * (col & 3);
+    // transposing reads: this lane addresses token 4grp + col/4 (+16, +32) of the tile, dims
+    // 16db + 4(col%4) .. +3 (through the row's piece rotation), and receives dim 16db + col of
+    // tokens 4grp .. 4grp+3 (16+...)
+    const uint8_t* vb = vtile;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -323,8 +376,9 @@ void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        const u32x2 lo = read_tr16(vb + ks * 32 * kRow + db * 32);
-        const u32x2 hi = read_tr16(vb + (ks * 32 + 16) * kRow + db * 32);
+        const int off = vr_base + ((2 * db * 16) ^ vr_x);
+        const u32x2 lo = read_tr16(vb + ks * 32 * kVRow + off);
+        const u32x2 hi = read_tr16(vb + (ks * 32 + 16) * kVRow + off);
         const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
         o[0][db] = Mfma16x16x32<dt>::run(vf, pb[0][ks], o[0][db]);
         o[1][db] = Mfma16x16x32<dt>::run(vf, pb[1][ks], o[1][db]);
@@ -333,33 +387,35 @@ void prefill_kernel(PrefillArgs a) {
   };
 
   // ---- walk the tiles ----------------------------------------------------------------------
-  // The block ids of tile i+2 are loaded while tile i is computed and turned into addresses only
-  // at step i+1, when the tile's own loads are issued, so no step waits on a table read.
+  // The block ids of tile i+2 are read (wave-uniform) while tile i is computed and used at step
+  // i+1, when the tile's loads are issued, so no step waits on a table read.
   if (n_steps > 0) {
-    load_tile(tile_of(table_block(ktok)));
-    // Every load so far (the queries and tile 0) completes here. Without this explicit wait the
-    // compiler's wait-count analysis, which cannot see that the query registers are complete
-    // once the first tile is, waits for every in-flight tile load before each step's first
-    // matrix instruction.
+    load_tile(k_s0, v_s0, table_block(ktok));
+    // Every load so far (the queries and tile 0) completes here: the tile's bytes are in LDS.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    store_tile(0, 0);
-    int kb_next = table_block(kTileT + ktok);
+    zero_tail(k_s0, v_s0, 0);
+    int kid_next = table_block(kTileT + ktok);
     __syncthreads();
     const int wp_lo = base_p + wj0;  // every column of the wave sees tokens 0..wp_lo
     const int wp_hi = base_p + wj1;  // no column sees a token past wp_hi
-    for (int step = 0; step < n_steps; ++step) {
+    // one step: compute the tile in (kc, vc) while the next one loads into (kn, vn)
+    auto step_at = [&](int step, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
       const int T0 = step * kTileT;
       const bool more = step + 1 < n_steps;
       if (more) {
-        load_tile(tile_of(kb_next));
-        kb_next = table_block(T0 + 2 * kTileT + ktok);
+        load_tile(kn, vn, kid_next);
+        kid_next = table_block(T0 + 2 * kTileT + ktok);
       }
-      if (w_active && T0 <= wp_hi) {
-        if (T0 + kTileT - 1 > wp_lo) compute(step & 1, T0, std::true_type{});
-        else compute(step & 1, T0, std::false_type{});
+      if (w_active && T0 <= wp_hi) compute(kc, vc, T0, T0 + kTileT - 1 > wp_lo);
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's part of the next tile landed
+        zero_tail(kn, vn, T0 + kTileT);
       }
-      if (more) store_tile((step + 1) & 1, T0 + kTileT);
       __syncthreads();
+    };
+    for (int step = 0; step < n_steps; step += 2) {
+      step_at(step, k_s0, v_s0, k_s1, v_s1);
+      if (step + 1 < n_steps) step_at(step + 1, k_s1, v_s1, k_s0, v_s0);
     }
   }
 
