@@ -51,6 +51,9 @@ constexpr float kRescaleSlackPf = 8.0f;      // log2 of the largest weight befor
 typedef float float2_t __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVmcnt0 = 0x0F70;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 static_assert(kPrefillThreads / 64 * kWaveQ == kTileQ, "four wavefronts of 32 queries");
 static_assert(kTileT == 64, "the token permutation below covers two 32-token MFMA steps");
 
@@ -65,11 +68,22 @@ __device__ __forceinline__ u32x2 read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// global_load_lds_dwordx4: 16 bytes from global address g straight into LDS, lane i's bytes
-// landing at lds + 16 * i (the LDS base is taken from the first lane); counted by vmcnt.
-__device__ __forceinline__ void load_lds16(const uint8_t* g, uint8_t* lds) {
+// buffer_load_dwordx4 ... lds: 16 bytes at byte offset voff of buffer r straight into LDS, lane
+// i's bytes landing at lds + 16 * i (the LDS base is taken from the first lane); counted by
+// vmcnt. The buffer form rather than global_load_lds: the compiler's wait-count model takes a
+// pending global (FLAT-encoded) LDS load as touching both memory counters and then makes every
+// LDS read wait for all earlier ones, which would serialise the operand reads with the matrix
+// products; the buffer form is tracked by vmcnt alone.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, int voff, uint8_t* lds) {
   typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, 0, 0, 0);
+}
+
+// Raw buffer resource over n bytes at p (dword 3: the gfx9 data-format field set to 32 bits;
+// offsets at or past n read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), static_cast<short>(0), n,
+                                           0x00020000);
 }
 
 // Maximum over lanes l, l^16, l^32, l^48 (the four rows of 16 lanes), in every lane: a
@@ -219,7 +233,7 @@ void prefill_kernel(PrefillArgs a) {
     t = t < ctx ? t : ctx - 1;
     return a.block_tables[table_row + t / B];
   };
-  // byte offset of (block b clamped into the pool, this KV head)
+  // byte offset of (block b clamped into the pool, this KV head); b is wave-uniform
   auto tile_of = [&](int b) -> int64_t {
     b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
     return (static_cast<int64_t>(b) * a.num_kv_heads + kvh) * G::kTileBytes;
@@ -232,23 +246,39 @@ void prefill_kernel(PrefillArgs a) {
     const int r = wave * 16 + i * kRPI + lane / kPPR;  // value row (token) this lane fills
     vl_off[i] = (r % B) * kVRow + ((lane % kPPR) ^ vswz(r)) * 16;
   }
-  // kid: this lane's table entry for its key token of the tile. The value rows of a wave load
-  // all lie in the block of the wavefront's tokens 0-7 (lanes col < 8) or 8-15 (col >= 8).
+  // kid: this lane's table entry for its key token of the tile. A wavefront's 16 tokens lie in
+  // the block of lane 0's token, and for B = 8 the second 8 (lanes col >= 8, value rows 8..15)
+  // in the block of lane 8's token; each block is one buffer resource (scalar registers) over
+  // that block's tile of this KV head.
   auto load_tile = [&](uint8_t* kdst, uint8_t* vdst, int kid) {
-    const int64_t kblk = tile_of(kid);
-    [[maybe_unused]] int64_t lo = kblk, hi = kblk;
-    if constexpr (B < 16) {
-      lo = tile_of(__shfl(kid, 0, 64));
-      hi = tile_of(__shfl(kid, 8, 64));
-    }
+    const int64_t lo = tile_of(__builtin_amdgcn_readfirstlane(kid));
+    const auto k_lo = tile_rsrc(a.k_pool + lo, G::kTileBytes);
+    const auto v_lo = tile_rsrc(a.v_pool + lo, G::kTileBytes);
+    if constexpr (B >= 16) {
 #pragma unroll
-    for (int c = 0; c < kKLoads; ++c)
-      load_lds16(a.k_pool + kblk + kl_off + c * G::kChunkRowBytes,
-                 kdst + (wave * kChunks + c) * 1024);
+      for (int c = 0; c < kKLoads; ++c)
+        load_lds16(k_lo, kl_off + c * G::kChunkRowBytes, kdst + (wave * kChunks + c) * 1024);
 #pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int64_t vblk = B >= 16 ? kblk : (i * kRPI >= 8 ? hi : lo);
-      load_lds16(a.v_pool + vblk + vl_off[i], vdst + (wave * 16 + i * kRPI) * kVRow);
+      for (int i = 0; i < kVLoads; ++i)
+        load_lds16(v_lo, vl_off[i], vdst + (wave * 16 + i * kRPI) * kVRow);
+    } else {
+      const int64_t hi = tile_of(__builtin_amdgcn_readlane(kid, 8));
+      const auto k_hi = tile_rsrc(a.k_pool + hi, G::kTileBytes);
+      const auto v_hi = tile_rsrc(a.v_pool + hi, G::kTileBytes);
+      // keys: each half of the 16 lanes of a column group reads its own block (lanes with
+      // col >= 8 under the second resource), into the same LDS slots as one wave load would
+      if (col < 8) {
+#pragma unroll
+        for (int c = 0; c < kKLoads; ++c)
+          load_lds16(k_lo, kl_off + c * G::kChunkRowBytes, kdst + (wave * kChunks + c) * 1024);
+      } else {
+#pragma unroll
+        for (int c = 0; c < kKLoads; ++c)
+          load_lds16(k_hi, kl_off + c * G::kChunkRowBytes, kdst + (wave * kChunks + c) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i)
+        load_lds16(i * kRPI >= 8 ? v_hi : v_lo, vl_off[i], vdst + (wave * 16 + i * kRPI) * kVRow);
     }
   };
   // after the wave's loads of tile T0 have landed: zeros over tokens at or past the context's
@@ -311,6 +341,15 @@ void prefill_kernel(PrefillArgs a) {
         st[1][tb] = Mfma16x16x32<dt>::run(kf, qf[1][c], st[1][tb]);
       }
     }
+    // schedule: each operand read is issued four reads ahead of its two products, so LDS
+    // latency hides behind matrix-core work instead of stalling it
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int r = 0; r < 4 * kChunks - 4; ++r) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
     __builtin_amdgcn_s_setprio(0);
     float mx[2];
 #pragma unroll
@@ -383,6 +422,18 @@ void prefill_kernel(PrefillArgs a) {
         o[0][db] = Mfma16x16x32<dt>::run(vf, pb[0][ks], o[0][db]);
         o[1][db] = Mfma16x16x32<dt>::run(vf, pb[1][ks], o[1][db]);
       }
+    // schedule: the value reads run four (ks, db) pairs ahead of their products
+    constexpr int kPairs = 2 * kDBlocks;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+#pragma unroll
+    for (int pr = 0; pr < kPairs - 4; ++pr) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
