@@ -193,6 +193,17 @@ void prefill_kernel(PrefillArgs a) {
   const int col = lane & 15;  // MFMA column (query) / row (token, dim) within a 16-block
   const int grp = lane >> 4;  // MFMA lane group: k values 8*grp .. 8*grp+7
   const int kvh = g_kv;
+  // The two workgroups on a CU put one wavefront on each SIMD. Raising both to the same
+  // priority in their matrix sections changes nothing (measured); raising them to different
+  // levels does: when both are in a matrix section the higher one issues first, the other falls
+  // a phase behind, and from then on one does its softmax while the other keeps the matrix
+  // pipe busy. The level comes from the parity of the workgroup's slot on its CU (TG_ID, bits
+  // 19:16 of HW_ID), which differs between two workgroups resident together.
+  const bool prio_hi = (__builtin_amdgcn_s_getreg((3 << 11) | (16 << 6) | 4) & 1) != 0;
+  auto mfma_priority = [&]() {
+    if (prio_hi) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(1);
+  };
 
   // ---- this wavefront's queries, held as B operands of S^T = K Q^T ------------------------
   const int wj0 = j0 + wave * kWaveQ;
@@ -329,7 +340,7 @@ void prefill_kernel(PrefillArgs a) {
     const uint8_t* kb = ktile + lane * 16;
     // matrix-core sections run at raised wave priority, so a wavefront that has its operands
     // keeps the matrix pipe fed while the SIMD's other wavefront does its softmax arithmetic
-    __builtin_amdgcn_s_setprio(1);
+    mfma_priority();
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       st[0][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -405,7 +416,7 @@ void prefill_kernel(PrefillArgs a) {
     // 16db + 4(col%4) .. +3 (through the row's piece rotation), and receives dim 16db + col of
     // tokens 4grp .. 4grp+3 (16+...)
     const uint8_t* vb = vtile;
-    __builtin_amdgcn_s_setprio(1);
+    mfma_priority();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       lacc[0] = Mfma16x16x32<dt>::run(ones, pb[0][ks], lacc[0]);
