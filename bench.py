@@ -496,13 +496,15 @@ def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=
     tpos = torch.from_numpy(batch.token_pos).to(dev)
     pairs = torch.from_numpy(batch.copy_pairs.reshape(-1)).to(dev)
     outs = [torch.empty_like(v["query"]) for v in sets]
+    # tables that share physical blocks (shared prompts) are read through the caches, and
+    # partitions that consecutive sequences share are computed once
+    shared = batch.shares_blocks
     ws_bytes = pa.pa_decode_workspace_bytes(sets[0]["k_pool"], cfg.num_seqs, cfg.num_q_heads,
-                                            cfg.head_dim, batch.max_context_len, part)
+                                            cfg.head_dim, batch.max_context_len, part,
+                                            shared_blocks=shared)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     kv_bytes = batch.kv_bytes()
     n_pairs = batch.copy_pairs.shape[0]
-    # tables that share physical blocks (shared prompts) are read through the caches
-    shared = batch.shares_blocks
 
     def step(k, ev=None):
         v = sets[k % len(sets)]

@@ -87,7 +87,13 @@ typedef enum {
  *   pa_decode call (shared prompt prefixes, parallel samples; [anal] §4, [dev] copy-on-write).
  *   pa_decode then reads key/value tiles through the caches so that the sharers reuse them.
  *   Without it every tile is read as a stream (non-temporal loads that do not allocate in the
- *   caches), which is faster when each tile is read once. Results are identical either way.
+ *   caches), which is faster when each tile is read once. With 16-bit pools, head_dim 128 and
+ *   more than one partition, it also has pa_decode compute a partition that consecutive
+ *   sequences share (the whole partition inside every sharer's context, the same physical block
+ *   ids in their tables) once for up to 8 of them: one workgroup scores all their queries
+ *   against each shared tile. The workspace then also holds a map of those groups
+ *   (pa_decode_workspace_bytes counts it when the descriptor carries the flag). Results agree
+ *   with the unshared computation within the stated tolerance; they are not bit-identical.
  */
 #define PA_CACHE_SHARED_BLOCKS 1u
 
@@ -135,6 +141,7 @@ PA_API pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, v
  * workgroups of one query head, 1024 when an even group size lets a workgroup serve 2 or 4
  * query heads). Returns 0 when
  * no workspace is needed (every context fits one partition) and (size_t)-1 for invalid sizes.
+ * The size depends on c->flags (PA_CACHE_SHARED_BLOCKS adds num_seqs * partitions int32s).
  */
 PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t partition_size);

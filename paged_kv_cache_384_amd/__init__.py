@@ -196,8 +196,8 @@ def pa_reshape_and_cache(key_cache, value_cache, key, value, block_tables, token
 
 def pa_decode_workspace_bytes(key_cache, num_seqs: int, num_q_heads: int, head_dim: int,
                               max_context_len: int, partition_size: int = 0,
-                              block_size: int | None = None) -> int:
-    d = _desc(key_cache, head_dim, block_size)
+                              block_size: int | None = None, shared_blocks: bool = False) -> int:
+    d = _desc(key_cache, head_dim, block_size, shared_blocks)
     n = lib().pa_decode_workspace_bytes(ctypes.byref(d), num_seqs, num_q_heads, max_context_len,
                                         partition_size)
     if n == ctypes.c_size_t(-1).value:
@@ -217,7 +217,7 @@ def _decode_call(fn_name, out, query, key_cache, value_cache, block_tables, cont
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
         raise ValueError("block_tables must be [num_seqs, max_blocks]; context_lens [num_seqs]")
     need = pa_decode_workspace_bytes(key_cache, S, Hq, head_dim, max_context_len, partition_size,
-                                     block_size)
+                                     block_size, shared_blocks)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else _vp(0)
@@ -238,7 +238,9 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     """out[s, h] = attention of query[s, h] over sequence s's paged cache (both stages).
 
     shared_blocks: some physical blocks are referenced by several sequences in this call, so the
-    key/value tiles are read through the caches instead of as a stream (same results).
+    key/value tiles are read through the caches instead of as a stream, and (16-bit pools,
+    head_dim 128) a partition that consecutive sequences share is computed once for up to 8 of
+    them; the workspace then also holds the map of those groups.
     Returns the workspace used (allocated with torch when none is given and one is needed).
     """
     return _decode_call("pa_decode", out, query, key_cache, value_cache, block_tables,

@@ -100,6 +100,8 @@ struct DecodePlan {
   int32_t part_tokens;
   int32_t num_parts;
   int32_t heads_per_wg;
+  bool share;             // partitions shared by consecutive sequences get one workgroup
+  size_t share_offset;    // byte offset of the share map in the workspace
   size_t workspace_bytes;
 };
 
@@ -126,6 +128,19 @@ pa_status plan_decode(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_he
   plan->workspace_bytes =
       np > 1 ? static_cast<size_t>(num_seqs) * num_q_heads * np * (c->head_dim + 2) * sizeof(float)
              : 0;
+  // Shared blocks declared, several partitions, and the matrix-core score path (16-bit pools,
+  // head_dim 128): the share plan after the partition states, 16-byte aligned: the map
+  // ([S][NP] int32), the two work lists (2 * S * NP int32) and their two counts
+  plan->share = (c->flags & PA_CACHE_SHARED_BLOCKS) != 0 && np > 1 && c->head_dim == 128 &&
+                (c->dtype == PA_F16 || c->dtype == PA_BF16);
+  plan->share_offset = (plan->workspace_bytes + 15) / 16 * 16;
+  if (plan->share) {
+    // the lists' unit counts (items x KV heads x head groups) are int64 in the kernels; the
+    // items themselves (s * NP + p) must fit int32
+    if (static_cast<int64_t>(num_seqs) * np > INT32_MAX / 4) return PA_ERR_SHAPE;
+    plan->workspace_bytes =
+        plan->share_offset + (3 * static_cast<size_t>(num_seqs) * np + 4) * sizeof(int32_t);
+  }
   return PA_OK;
 }
 
@@ -194,15 +209,37 @@ pa_status decode_impl(int stages, bool paged, const pa_cache_desc* c, const void
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   a.stream_kv = (c->flags & PA_CACHE_SHARED_BLOCKS) == 0;
   a.paged = paged;
+  a.share_map = nullptr;
+  a.share_list = nullptr;
+  a.share_counts = nullptr;
+  if (plan.share && paged) {
+    const int64_t items = static_cast<int64_t>(num_seqs) * plan.num_parts;
+    a.share_map =
+        reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + plan.share_offset);
+    a.share_list = a.share_map + items;
+    a.share_counts = a.share_list + 2 * items;
+  }
 
   const DType dt = static_cast<DType>(c->dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stages & kStageAttention) {
     hipError_t e;
-    switch (c->block_size) {
-      case 8: e = pa::launch_decode_attention_b8(dt, c->head_dim, a, s); break;
-      case 32: e = pa::launch_decode_attention_b32(dt, c->head_dim, a, s); break;
-      default: e = pa::launch_decode_attention_b16(dt, c->head_dim, a, s); break;
+    if (a.share_map != nullptr) {
+      // the share plan, then the attention over its two lists
+      e = pa::launch_share_plan(a, c->block_size, s);
+      if (e == hipSuccess) {
+        switch (c->block_size) {
+          case 8: e = pa::launch_decode_attention_shared_b8(dt, a, s); break;
+          case 32: e = pa::launch_decode_attention_shared_b32(dt, a, s); break;
+          default: e = pa::launch_decode_attention_shared_b16(dt, a, s); break;
+        }
+      }
+    } else {
+      switch (c->block_size) {
+        case 8: e = pa::launch_decode_attention_b8(dt, c->head_dim, a, s); break;
+        case 32: e = pa::launch_decode_attention_b32(dt, c->head_dim, a, s); break;
+        default: e = pa::launch_decode_attention_b16(dt, c->head_dim, a, s); break;
+      }
     }
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }

@@ -244,30 +244,28 @@ struct MfmaBlockStep {
   }
 };
 
-template <DType dt, int D, int B, int NH, bool kStream, bool kPaged>
-__global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
+// Work item modes of the decode kernel: kGrid, one workgroup per (KV head, sequence, head group,
+// partition) as the grid's blocks; kList and kListSeqRows, a persistent loop over the items of
+// the share plan's lists (partitions a sequence computes itself; partitions shared by a group of
+// sequences, whose NH score columns are then one query head of the group's sequences).
+enum DecodeMode : int { kGrid = 0, kList = 1, kListSeqRows = 2 };
+
+// One work item: (KV head kvh, sequence s, head group hg, partition part). kSeqRows: the NH
+// score columns are head kvh * group + hg of sequences s .. s + rows - 1, which share this
+// partition's blocks, instead of NH query heads of sequence s.
+template <DType dt, int D, int B, int NH, bool kStream, bool kPaged, bool kSeqRows>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int kvh, int s, int hg, int part,
+                                            int rows, float (&red_s)[kDecodeThreads / 64][NH][D],
+                                            float (&m_s)[kDecodeThreads / 64][NH],
+                                            float (&l_s)[kDecodeThreads / 64][NH]) {
   using G = TileGeom<dt, D, B>;
   constexpr int kLoads = G::kLoads;
   constexpr int kEpp = G::kEpp;
   constexpr int kPiecesPerRow = G::kPiecesPerRow;
   constexpr int kWaves = kDecodeThreads / 64;
-
-  __shared__ float red_s[kWaves][NH][D];
-  __shared__ float m_s[kWaves][NH];
-  __shared__ float l_s[kWaves][NH];
-
-  // ---- which work item -------------------------------------------------------------------
-  int r = xcd_logical_index();
-  const int hg = r % a.head_groups;
-  r /= a.head_groups;
-  const int s = r % a.num_seqs;
-  r /= a.num_seqs;
-  const int part = r % a.num_parts;
-  const int kvh = r / a.num_parts;
-
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int h0 = kvh * a.group + hg * NH;
+  const int h0 = kSeqRows ? kvh * a.group + hg : kvh * a.group + hg * NH;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -371,10 +369,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   [[maybe_unused]] u32x4 qv[kMfma ? 1 : NH][kLoads];
   if constexpr (kMfma) {
     const int qh = lane & 15;
+    // column qh: query head h0 + qh of sequence s, or (seq rows) head h0 of sequence s + qh
+    const uint8_t* qrow =
+        kSeqRows ? a.query + (static_cast<int64_t>(s + qh) * a.num_q_heads + h0) * G::kRowBytes
+                 : qbase + qh * G::kRowBytes;
 #pragma unroll
     for (int c = 0; c < kLoads; ++c)
-      qm[c] = qh < NH ? load16(qbase + qh * G::kRowBytes + c * 64 + 16 * (lane >> 4))
-                      : u32x4{0u, 0u, 0u, 0u};
+      qm[c] = qh < rows ? load16(qrow + c * 64 + 16 * (lane >> 4)) : u32x4{0u, 0u, 0u, 0u};
   } else {
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh)
@@ -488,6 +489,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
   for (int i = tid; i < NH * D; i += kDecodeThreads) {
     const int hh = i / D;
     const int col = i % D;
+    // row hh: (sequence s, head h0 + hh), or (seq rows) (sequence s + hh, head h0), which has
+    // its own context length and so its own partition count
+    [[maybe_unused]] int row_parts = nparts;
+    if constexpr (kSeqRows) {
+      if (hh >= rows) break;
+      int c = a.context_lens[s + hh];
+      c = c < 0 ? 0 : (c > a.max_ctx ? a.max_ctx : c);
+      row_parts = (c + a.part_tokens - 1) / a.part_tokens;
+    }
+    const int64_t row = kSeqRows ? static_cast<int64_t>(s + hh) * a.num_q_heads + h0 : sh0 + hh;
     // wave 0 always holds block 0, so the maximum is finite; idle wavefronts (m = -inf,
     // sums 0) get weight 0
     float M = m_s[0][hh];
@@ -500,15 +511,51 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(Decode
       o = __builtin_fmaf(c, red_s[w][hh][col], o);
       L = __builtin_fmaf(c, l_s[w][hh], L);
     }
-    if (nparts == 1) {
-      Narrow<dt>::store(a.out + ((sh0 + hh) * D + col) * G::kEsz, o / L);
+    if (row_parts == 1) {
+      Narrow<dt>::store(a.out + (row * D + col) * G::kEsz, o / L);
     } else {
-      const int64_t st = (sh0 + hh) * a.num_parts + part;
+      const int64_t st = row * a.num_parts + part;
       a.ws_acc[st * D + col] = o;
       if (col == 0) {
         a.ws_m[st] = M;
         a.ws_l[st] = L;
       }
+    }
+  }
+}
+
+template <DType dt, int D, int B, int NH, bool kStream, bool kPaged, int kMode = kGrid>
+__global__ __launch_bounds__(kDecodeThreads) void decode_attention_kernel(DecodeArgs a) {
+  constexpr int kWaves = kDecodeThreads / 64;
+  __shared__ float red_s[kWaves][NH][D];
+  __shared__ float m_s[kWaves][NH];
+  __shared__ float l_s[kWaves][NH];
+  if constexpr (kMode == kGrid) {
+    int r = xcd_logical_index();
+    const int hg = r % a.head_groups;
+    r /= a.head_groups;
+    const int s = r % a.num_seqs;
+    r /= a.num_seqs;
+    const int part = r % a.num_parts;
+    const int kvh = r / a.num_parts;
+    decode_item<dt, D, B, NH, kStream, kPaged, false>(a, kvh, s, hg, part, NH, red_s, m_s, l_s);
+  } else {
+    // the share plan's list of (sequence, partition) items, each for every KV head and head
+    // group; the counts were written by the plan kernel earlier on this stream
+    constexpr bool kSeq = kMode == kListSeqRows;
+    const int groups = kSeq ? a.group : a.head_groups;
+    const int64_t per = static_cast<int64_t>(a.num_kv_heads) * groups;
+    const int32_t* list = a.share_list + (kSeq ? static_cast<int64_t>(a.num_seqs) * a.num_parts : 0);
+    const int64_t units = static_cast<int64_t>(a.share_counts[kSeq ? 1 : 0]) * per;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+      const int item = list[u / per];
+      const int rem = static_cast<int>(u % per);
+      const int s = item / a.num_parts;
+      const int part = item % a.num_parts;
+      const int rows = kSeq ? a.share_map[item] : NH;
+      decode_item<dt, D, B, NH, kStream, kPaged, kSeq>(a, rem / groups, s, rem % groups, part,
+                                                        rows, red_s, m_s, l_s);
+      __syncthreads();  // the next item reuses the LDS arrays
     }
   }
 }
@@ -540,6 +587,43 @@ hipError_t launch_attn_nh(const DecodeArgs& a, hipStream_t stream) {
     case 4: return launch_attn<dt, D, B, 4>(a, stream);
     case 2: return launch_attn<dt, D, B, 2>(a, stream);
     default: return launch_attn<dt, D, B, 1>(a, stream);
+  }
+}
+
+// With a share plan: the partitions sequences compute themselves, and those shared by groups
+// of sequences, each as a persistent loop over its list (only 16-bit pools with head_dim 128
+// get a plan). Grids: about what the CUs hold at once.
+template <DType dt, int B, int NH>
+hipError_t launch_attn_list(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t most = static_cast<int64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads;
+  const unsigned own = static_cast<unsigned>(most * a.head_groups < 2048 ? most * a.head_groups : 2048);
+  const unsigned shared = static_cast<unsigned>(most * a.group < 1024 ? most * a.group : 1024);
+  hipLaunchKernelGGL((decode_attention_kernel<dt, 128, B, kShareMax, false, true, kListSeqRows>),
+                     dim3(shared), dim3(kDecodeThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the partitions a sequence computes itself are the ones no other sequence in the call
+  // shares in full: streamed (non-temporal loads, two blocks in flight for one head)
+  hipLaunchKernelGGL((decode_attention_kernel<dt, 128, B, NH, true, true, kList>), dim3(own),
+                     dim3(kDecodeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <DType dt, int B>
+hipError_t launch_attn_shared(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.heads_per_wg) {
+    case 4: return launch_attn_list<dt, B, 4>(a, stream);
+    case 2: return launch_attn_list<dt, B, 2>(a, stream);
+    default: return launch_attn_list<dt, B, 1>(a, stream);
+  }
+}
+
+template <int B>
+hipError_t launch_attn_shared_block(DType dt, const DecodeArgs& a, hipStream_t stream) {
+  switch (dt) {
+    case DType::F16: return launch_attn_shared<DType::F16, B>(a, stream);
+    case DType::BF16: return launch_attn_shared<DType::BF16, B>(a, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -8,4 +8,8 @@ hipError_t launch_decode_attention_b32(DType dt, int head_dim, const DecodeArgs&
   return launch_attn_block<32>(dt, head_dim, a, stream);
 }
 
+hipError_t launch_decode_attention_shared_b32(DType dt, const DecodeArgs& a, hipStream_t stream) {
+  return launch_attn_shared_block<32>(dt, a, stream);
+}
+
 }  // namespace pa

@@ -8,4 +8,8 @@ hipError_t launch_decode_attention_b8(DType dt, int head_dim, const DecodeArgs& 
   return launch_attn_block<8>(dt, head_dim, a, stream);
 }
 
+hipError_t launch_decode_attention_shared_b8(DType dt, const DecodeArgs& a, hipStream_t stream) {
+  return launch_attn_shared_block<8>(dt, a, stream);
+}
+
 }  // namespace pa

@@ -109,7 +109,20 @@ struct DecodeArgs {
   bool stream_kv;       // read key/value tiles with non-temporal (streaming) loads
   bool paged;           // false: no table, sequence s's block j is physical block
                         // s * max_blocks + j (the contiguous twin)
+  // The share plan (all nullptr: no sharing). share_map [S][NP], entry (s, p): 1 when sequence
+  // s computes partition p itself, n >= 2 when s leads a group of n sequences s .. s+n-1 whose
+  // partition p is full and made of the same physical blocks (computed once for all of them),
+  // 0 when s is in such a group led by an earlier sequence. share_list: the items s * NP + p
+  // sequences compute themselves (partitions inside their contexts, and partition 0 of an
+  // empty context), then from offset S * NP the items of group leaders; share_counts: their
+  // numbers (own, shared), counted up by the plan kernel from zero.
+  int32_t* share_map;
+  int32_t* share_list;
+  int32_t* share_counts;
 };
+
+// Sequences one shared-partition workgroup serves; groups are cut at multiples of this index.
+constexpr int kShareMax = 8;
 
 constexpr int kPrefillThreads = 256;       // four wavefronts per prefill workgroup
 constexpr int kPrefillTileQueries = 128;  // queries one prefill workgroup owns
@@ -157,6 +170,12 @@ hipError_t launch_decode_attention_b16(DType dt, int head_dim, const DecodeArgs&
 hipError_t launch_decode_attention_b32(DType dt, int head_dim, const DecodeArgs& a,
                                        hipStream_t stream);
 hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream);
+// the share plan (see DecodeArgs), then the attention over its two lists (16-bit pools with
+// head_dim 128 only), which replaces the grid launch of launch_decode_attention_b*
+hipError_t launch_share_plan(const DecodeArgs& a, int block_size, hipStream_t stream);
+hipError_t launch_decode_attention_shared_b8(DType dt, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_attention_shared_b16(DType dt, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_attention_shared_b32(DType dt, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(DType dt, int head_dim, int block_size, const PrefillArgs& a,
                           hipStream_t stream);
 

@@ -132,6 +132,101 @@ static hipError_t launch_red(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// The share plan: which partitions consecutive sequences share, and the work lists.
+//
+// Source: "PagedAttention 심층 분석 — LLM KV 캐시 메모리 관리" (ryotta.opik.net), §4: sequences
+// of one request (parallel samples, a common prompt) point their tables at the same physical
+// blocks. A partition whose blocks are the same in two sequences holds the same keys and values
+// for both, so one workgroup can score both sequences' queries against it and leave each its
+// own partition state (the merge combines states in any grouping, as above).
+//
+// Sequence t joins the group of t - 1 on partition p when both contexts cover the whole
+// partition, their table entries for it are equal, and t is not a multiple of kShareMax; groups
+// are therefore cut at multiples of kShareMax, so each window of kShareMax sequences is planned
+// on its own: one workgroup per (window, partition), wavefront k comparing the table entries of
+// sequence 8w + k with those of its predecessor (lanes over the entries), then one thread
+// writing the window's map entries and appending its items to the lists.
+// ------------------------------------------------------------------------------------------
+constexpr int kPlanThreads = kShareMax * 64;
+
+__global__ void share_clear_kernel(int32_t* counts) {
+  if (threadIdx.x < 2) counts[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void share_plan_kernel(DecodeArgs a, int block_size) {
+  __shared__ int full_s[kShareMax];
+  __shared__ int join_s[kShareMax];
+  __shared__ int ctx_s[kShareMax];
+  const int windows = (a.num_seqs + kShareMax - 1) / kShareMax;
+  const int w = static_cast<int>(blockIdx.x % windows);
+  const int p = static_cast<int>(blockIdx.x / windows);
+  const int k = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = w * kShareMax + k;
+  const int end = (p + 1) * a.part_tokens;
+  const int per_part = a.part_tokens / block_size;  // table entries of one partition
+  auto ctx_of = [&](int q) {
+    const int c = a.context_lens[q];
+    return c < 0 ? 0 : (c > a.max_ctx ? a.max_ctx : c);
+  };
+  const int ct = t < a.num_seqs ? ctx_of(t) : 0;
+  const bool full = ct >= end;  // then end <= max_ctx <= max_blocks * block_size
+  bool join = false;
+  if (k != 0 && full && ctx_of(t - 1) >= end) {
+    const int32_t* x = a.block_tables + static_cast<int64_t>(t - 1) * a.max_blocks +
+                       static_cast<int64_t>(p) * per_part;
+    const int32_t* y = x + a.max_blocks;
+    bool differ = false;
+    for (int j = lane; j < per_part; j += 64) differ |= x[j] != y[j];
+    join = __builtin_amdgcn_ballot_w64(differ) == 0;
+  }
+  if (lane == 0) {
+    full_s[k] = full;
+    join_s[k] = join;
+    ctx_s[k] = ct;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int own[kShareMax], lead[kShareMax];
+  int n_own = 0, n_lead = 0;
+  for (int q = 0; q < kShareMax && w * kShareMax + q < a.num_seqs; ++q) {
+    const int item = (w * kShareMax + q) * a.num_parts + p;
+    int n = 1;
+    if (full_s[q]) {
+      if (join_s[q]) {
+        n = 0;
+      } else {
+        while (q + n < kShareMax && join_s[q + n]) ++n;
+      }
+    }
+    a.share_map[item] = n;
+    if (n >= 2) lead[n_lead++] = item;
+    // a sequence computes the partitions inside its context itself (and partition 0 of an
+    // empty context, which writes zeros)
+    if (n == 1 && (p * a.part_tokens < ctx_s[q] || p == 0)) own[n_own++] = item;
+  }
+  const int64_t lead_base = static_cast<int64_t>(a.num_seqs) * a.num_parts;
+  if (n_own > 0) {
+    const int at = atomicAdd(&a.share_counts[0], n_own);
+    for (int q = 0; q < n_own; ++q) a.share_list[at + q] = own[q];
+  }
+  if (n_lead > 0) {
+    const int at = atomicAdd(&a.share_counts[1], n_lead);
+    for (int q = 0; q < n_lead; ++q) a.share_list[lead_base + at + q] = lead[q];
+  }
+}
+
+hipError_t launch_share_plan(const DecodeArgs& a, int block_size, hipStream_t stream) {
+  hipLaunchKernelGGL(share_clear_kernel, dim3(1), dim3(64), 0, stream, a.share_counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>((a.num_seqs + kShareMax - 1) / kShareMax) * a.num_parts;
+  hipLaunchKernelGGL(share_plan_kernel, dim3(static_cast<unsigned>(n)), dim3(kPlanThreads), 0,
+                     stream, a, block_size);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_reduce(DType dt, int head_dim, const DecodeArgs& a, hipStream_t stream) {
   if (a.num_parts <= 1) return hipSuccess;
   switch (dt) {

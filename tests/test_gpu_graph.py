@@ -34,11 +34,12 @@ def test_graph_replay_matches_eager(name, over):
     tpos = torch.from_numpy(batch.token_pos).to(dev)
     pairs = torch.from_numpy(batch.copy_pairs.reshape(-1)).to(dev)
     part = 64
+    shared = batch.shares_blocks
     ws_bytes = pa.pa_decode_workspace_bytes(vals["k_pool"], cfg.num_seqs, cfg.num_q_heads,
-                                            cfg.head_dim, batch.max_context_len, part)
+                                            cfg.head_dim, batch.max_context_len, part,
+                                            shared_blocks=shared)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty_like(vals["query"])
-    shared = batch.shares_blocks
 
     def step(o):
         if batch.copy_pairs.shape[0]:
