@@ -41,8 +41,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# the attention stage's kernels: the decode kernel, and the share plan (shared-prefix batches)
 KERNEL_SOURCES = ["paged_kv_cache_384_amd/csrc/pa_attention.h",
-                  "paged_kv_cache_384_amd/csrc/pa_device.h"]
+                  "paged_kv_cache_384_amd/csrc/pa_device.h",
+                  "paged_kv_cache_384_amd/csrc/pa_reduce.hip"]
 
 
 def kernel_source_hash() -> str:
