@@ -474,7 +474,7 @@ def tile_read_reference(sets, nbytes, tile_bytes, steps, stream):
 
 
 def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=True,
-                paging=False, swap=False):
+                paging=False, swap=False, kv_head_shards=1):
     """One decode workload: K eager steps with HIP events around every kernel, then K
     graph-replayed steps, the CPU oracle (one thread on a bounded sample, and every host core on
     the whole batch), and the optional paging-overhead and swap measurements. Returns the
@@ -487,6 +487,17 @@ def decode_rate(name, args, dev, stream, *, part_override=-1, block_size=0, cpu=
     cfg = wl.CONFIGS[name]
     if block_size and block_size != cfg.block_size:
         cfg = wl.config(name, block_size=block_size, num_blocks=0)
+    if kv_head_shards > 1:
+        # one GPU's share when the KV heads (and their query heads) are split over that many
+        # GPUs: the same sequences, tables and block count, 1/shards of every block's heads
+        if cfg.num_kv_heads % kv_head_shards:
+            raise SystemExit(f"{name}: {cfg.num_kv_heads} KV heads do not split {kv_head_shards} ways")
+        from dataclasses import replace
+        cfg = replace(cfg, name=f"{cfg.name}_kvshard{kv_head_shards}",
+                      num_q_heads=cfg.num_q_heads // kv_head_shards,
+                      num_kv_heads=cfg.num_kv_heads // kv_head_shards,
+                      description=f"{cfg.description}; one GPU's share of its KV heads split "
+                                  f"{kv_head_shards} ways")
     part = cfg.partition_size if part_override < 0 else part_override
     batch = wl.build_batch(cfg)
     print(f"[bench] {cfg.name}: {cfg.description}", file=sys.stderr, flush=True)
@@ -671,6 +682,10 @@ def main():
                     help="partition size in tokens for the headline workload; -1 = the "
                          "workload's own setting")
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--kv-head-shards", type=int, default=1,
+                    help="time one GPU's share of the --config batch when its KV heads are split "
+                         "this many ways (tensor parallelism over heads); the one-GPU run "
+                         "measures that share at its real shape")
     ap.add_argument("--block-size", type=int, default=0,
                     help="run the headline workload at this block size (8, 16 or 32) instead of "
                          "its own; the pool is then sized for the blocks in use (1.25x)")
@@ -726,7 +741,7 @@ def main():
     cpu = not args.no_cpu_baseline
     head = decode_rate(args.config, args, dev, stream, part_override=args.partition,
                        block_size=args.block_size, cpu=cpu, paging=args.paging_overhead,
-                       swap=args.swap)
+                       swap=args.swap, kv_head_shards=args.kv_head_shards)
     if args.copy_calibration:
         copy_calibration(dev)
     others = [decode_rate(n, args, dev, stream, cpu=cpu)
