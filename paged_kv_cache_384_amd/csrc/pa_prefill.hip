@@ -15,8 +15,8 @@
 // head); each wavefront owns 32 of them as two 16-query MFMA columns. The workgroup walks the
 // sequence's tokens in tiles of 64, from token 0 to the last position its queries can see:
 //   * the tile's keys and values are gathered through the block table straight into LDS by
-//     global_load_lds_dwordx4 (no trip through registers; double buffered, the next tile's loads
-//     in flight while the current one is computed). Keys land in the order the matrix-core
+//     buffer_load_dwordx4 ... lds (no trip through registers; double buffered, the next tile's
+//     loads in flight while the current one is computed). Keys land in the order the matrix-core
 //     operand reads want them; values in token rows whose 16-byte pieces are rotated by the
 //     token, so the transposing reads below meet every bank once;
 //   * each wavefront forms S^T = K Q^T: A = 16 tokens x 32 dims read from LDS, B = its queries
