@@ -18,3 +18,17 @@ def test_full_size(name):
     log(f"    max_abs_err={r['max_abs_err']:.3g} max err/bar={r['max_err_over_bar']:.3g} "
         f"allowance elements={r['allowance_elems']} max|o|={r['max_abs_out']:.3g} "
         f"oracle {r['oracle_s']:.1f}s prep {r['prep_s']:.1f}s")
+
+
+@pytest.mark.parametrize("name", ["opt13b_fp16", "gqa_bf16", "long_bf16"])
+def test_kv_head_shard(name):
+    """One GPU's share of the batch when its KV heads are split 8 ways (what bench.py
+    --kv-head-shards 8 times): the same sequences, tables and pool with 1/8 of the heads, so far
+    fewer workgroups than the whole batch launches."""
+    from dataclasses import replace
+    full = wl.CONFIGS[name]
+    cfg = replace(full, name=f"{name}_kvshard8", num_q_heads=full.num_q_heads // 8,
+                  num_kv_heads=full.num_kv_heads // 8)
+    log(f"[full] {cfg.name}: {cfg.num_q_heads} query heads over {cfg.num_kv_heads} KV heads")
+    r = run_step(cfg, partition_size=cfg.partition_size, device_values=True)
+    log(f"    max_abs_err={r['max_abs_err']:.3g} max err/bar={r['max_err_over_bar']:.3g}")
