@@ -141,7 +141,9 @@ PA_API pa_status pa_reshape_and_cache(const pa_cache_desc* c, void* key_cache, v
  * workgroups of one query head, 1024 when an even group size lets a workgroup serve 2 or 4
  * query heads). Returns 0 when
  * no workspace is needed (every context fits one partition) and (size_t)-1 for invalid sizes.
- * The size depends on c->flags (PA_CACHE_SHARED_BLOCKS adds num_seqs * partitions int32s).
+ * The size depends on c->flags: with PA_CACHE_SHARED_BLOCKS, 16-bit pools, head_dim 128 and more
+ * than one partition, the share plan follows the partition states (16-byte aligned):
+ * 3 * num_seqs * partitions + 4 int32s (the share map, two work lists and their counts).
  */
 PA_API size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t partition_size);
